@@ -1,0 +1,176 @@
+"""fp64 CPU oracle for the Orthrus decode step.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may use this package; the product path
+(``ar_shared_kv_amd``) never imports it, and the two share no code.
+
+The arithmetic lives in ``orthrus_oracle.c`` (plain C, fp64, compiled with
+gcc); this module only marshals numpy arrays.  Each function cites the passage
+of the pages it follows (see the C file's header for the source list):
+
+* ``block_attn``  -- shared-KV block attention, bidirectional (diffusion view)
+  or causal (AR verification) inside the block; summary §2.1-§2.3.
+* ``argmax_rows`` -- greedy prediction per row, lowest index on ties;
+  summary §2.3 step 3.
+* ``consensus``   -- left-to-right exact consensus; summary §2.3 step 3.
+* ``kv_append``   -- commit of the accepted rows' KV; summary §2.3 step 3 and
+  the agents-report core-design section.
+
+Parity pins: every function is pinned by the ``-m "not gpu"`` tests in
+``tests/test_oracle_*.py`` (library routines, closed forms, invariants and
+brute force); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "orthrus_oracle.c")
+_LIB = os.path.join(_HERE, "liborthrus_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+CONTIGUOUS, PAGED = 0, 1
+BIDIR, CAUSAL = 0, 1
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (portable flags, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            lib = ctypes.CDLL(build())
+            P, I, L, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_double
+            lib.oracle_block_attn.argtypes = [P, P, P, I, L, I, P, I, I, P, P, P,
+                                              I, I, I, I, I, I, D, P, P]
+            lib.oracle_block_attn.restype = I
+            lib.oracle_argmax_rows.argtypes = [P, L, L, P]
+            lib.oracle_argmax_rows.restype = I
+            lib.oracle_consensus.argtypes = [P, P, I, I, P, P, P, P, P]
+            lib.oracle_consensus.restype = None
+            lib.oracle_kv_append.argtypes = [P, P, I, L, I, P, I, I, P, P, P, P, P,
+                                             I, I, I, I, I, I, L, L]
+            lib.oracle_kv_append.restype = I
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = I
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def block_attn(q, k_cache, v_cache, k_blk, v_blk, lens, *, mask, scale,
+               layout=CONTIGUOUS, page_table=None, page_size=16):
+    """Block attention of one layer in fp64.
+
+    q, k_blk, v_blk: [B, K, H, D]; contiguous caches [B, Hkv, cap, D] or paged
+    caches [num_pages, Hkv, page_size, D] with page_table [B, max_pages].
+    Returns (out [B, K, Hq, D], lse [B, Hq, K]) as float64 arrays.
+    """
+    q, kc, vc, kb, vb = map(_f64, (q, k_cache, v_cache, k_blk, v_blk))
+    lens = _i32(lens)
+    B, K, Hq, D = q.shape
+    Hkv = kb.shape[2]
+    if layout == CONTIGUOUS:
+        cap, num_pages, max_pages, pt = kc.shape[2], 0, 0, None
+    else:
+        pt = _i32(page_table)
+        cap, num_pages, max_pages = 0, kc.shape[0], pt.shape[1]
+        page_size = kc.shape[2]
+    out = np.empty((B, K, Hq, D), np.float64)
+    lse = np.empty((B, Hq, K), np.float64)
+    rc = _load().oracle_block_attn(_ptr(q), _ptr(kc), _ptr(vc), layout, cap, page_size,
+                                   _ptr(pt), max_pages, num_pages, _ptr(lens), _ptr(kb),
+                                   _ptr(vb), B, K, Hq, Hkv, D, mask, float(scale),
+                                   _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_block_attn rejected its arguments")
+    return out, lse
+
+
+def argmax_rows(x):
+    """Row argmax of x[..., V] (lowest index on ties); returns int32 [...]."""
+    x = _f64(x)
+    V = x.shape[-1]
+    rows = x.size // V
+    idx = np.empty(rows, np.int32)
+    if _load().oracle_argmax_rows(_ptr(x), rows, V, _ptr(idx)) != 0:
+        raise ValueError("argmax undefined: NaN in logits")
+    return idx.reshape(x.shape[:-1])
+
+
+def consensus(d_tok, a_tok):
+    """Exact consensus over [B, K] token arrays.
+
+    Returns dict with j, n, emit_off [B+1], emitted [sum n], next_anchor.
+    """
+    d, a = _i32(d_tok), _i32(a_tok)
+    B, K = d.shape
+    j = np.empty(B, np.int32)
+    n = np.empty(B, np.int32)
+    off = np.empty(B + 1, np.int32)
+    emitted = np.empty(B * K, np.int32)
+    anchor = np.empty(B, np.int32)
+    _load().oracle_consensus(_ptr(d), _ptr(a), B, K, _ptr(j), _ptr(n), _ptr(off),
+                             _ptr(emitted), _ptr(anchor))
+    return {"j": j, "n": n, "emit_off": off, "emitted": emitted[: off[B]].copy(),
+            "next_anchor": anchor}
+
+
+def kv_append(k_cache, v_cache, k_blk, v_blk, n, lens, *, layout=CONTIGUOUS,
+              page_table=None):
+    """Append accepted AR block rows into copies of the caches.
+
+    k_cache/v_cache: [layers, ...cache layout...] numpy arrays of any element
+    type (copied as bytes); k_blk/v_blk: [layers, B, K, Hkv, D].
+    Returns (k_cache', v_cache', lens_out).
+    """
+    kc = np.array(k_cache, copy=True, order="C")
+    vc = np.array(v_cache, copy=True, order="C")
+    kb = np.ascontiguousarray(k_blk)
+    vb = np.ascontiguousarray(v_blk)
+    if kb.dtype != kc.dtype or vb.dtype != kc.dtype or vc.dtype != kc.dtype:
+        raise ValueError("cache and block element types differ")
+    layers, B, K, Hkv, D = kb.shape
+    n, lens = _i32(n), _i32(lens)
+    if layout == CONTIGUOUS:
+        cap, page_size, num_pages, max_pages, pt = kc.shape[3], 16, 0, 0, None
+    else:
+        pt = _i32(page_table)
+        cap, num_pages, page_size, max_pages = 0, kc.shape[1], kc.shape[3], pt.shape[1]
+    lens_out = np.empty(B, np.int32)
+    rc = _load().oracle_kv_append(_ptr(kc), _ptr(vc), layout, cap, page_size, _ptr(pt),
+                                  max_pages, num_pages, _ptr(lens), _ptr(kb), _ptr(vb),
+                                  _ptr(n), _ptr(lens_out), B, K, Hkv, D, kc.itemsize,
+                                  layers, kc[0].size, kb[0].size)
+    if rc != 0:
+        raise ValueError("oracle_kv_append rejected its arguments")
+    return kc, vc, lens_out

@@ -1,0 +1,247 @@
+/*
+ * Orthrus decode-step oracle: a plain, slow fp64 CPU implementation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no code, header or table with the HIP
+ * library.
+ *
+ * Sources (the pages the method is described on):
+ *   [SUM]  "Orthrus: Memory-Efficient Parallel Token Generation via
+ *          Dual-View Diffusion", gist.science technical summary:
+ *          §2.1 dual-view attention over one shared KV cache,
+ *          §2.2 block masking (anchor + K-1 mask slots, bidirectional block),
+ *          §2.3 inference: parallel projection, AR verification, left-to-right
+ *               consensus and commit.
+ *   [ABS]  the paper's abstract (chatpaper.ai page): both views read the same
+ *          KV cache; exact consensus makes inference lossless.
+ *   [REP]  agents-report.net commentary, section on the core design: accepted
+ *          tokens' KV state is appended to the shared cache.
+ *
+ * Every floating-point step is fp64 on the exact input values (bf16 and fp32
+ * inputs convert to fp64 without rounding).  No blocking, fusion or
+ * reordering: each output is its definition written out.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { O_CONTIGUOUS = 0, O_PAGED = 1 };
+enum { O_BIDIR = 0, O_CAUSAL = 1 };
+
+/* Address of cache row t of request b, KV head g.
+ * Contiguous layout [B][Hkv][cap][D]; paged layout [num_pages][Hkv][page][D]
+ * where logical token t of request b lives in page page_table[b][t / page],
+ * slot t % page.  Returns NULL if the page table points out of range. */
+static const double *cache_row(const double *base, int layout, long cap,
+                               int page_size, const int32_t *page_table,
+                               int max_pages, int num_pages, int Hkv, int D,
+                               int b, int g, long t)
+{
+    if (layout == O_CONTIGUOUS)
+        return base + (((long)b * Hkv + g) * cap + t) * D;
+    long lp = t / page_size;
+    if (lp >= max_pages) return NULL;
+    int32_t page = page_table[(long)b * max_pages + lp];
+    if (page < 0 || page >= num_pages) return NULL;
+    return base + (((long)page * Hkv + g) * page_size + t % page_size) * D;
+}
+
+/*
+ * Shared-KV block attention for one layer.  [SUM] §2.1-§2.3, [REP].
+ *
+ * For request b, query head h (KV head g = h / (Hq/Hkv)) and block row i, the
+ * key set is every cache row 0..lens[b]-1 of head g, plus block rows
+ *   j = 0..K-1  (mask BIDIR, the diffusion view: the block attends to itself
+ *                bidirectionally)
+ *   j = 0..i    (mask CAUSAL, the AR verification view: causal, row i sees
+ *                itself)
+ * Scores s_t = scale * <q, k_t>; out = sum_t exp(s_t - m) v_t / sum_t
+ * exp(s_t - m) with m = max_t s_t; lse = m + log(sum_t exp(s_t - m)).
+ *
+ * q, k_blk, v_blk, out: [B][K][H][D]; lse: [B][Hq][K] (may be NULL).
+ * Returns 0, or -1 on a bad argument / page index.
+ */
+int oracle_block_attn(const double *q, const double *k_cache,
+                      const double *v_cache, int layout, long cap,
+                      int page_size, const int32_t *page_table, int max_pages,
+                      int num_pages, const int32_t *lens, const double *k_blk,
+                      const double *v_blk, int B, int K, int Hq, int Hkv,
+                      int D, int mask, double scale, double *out, double *lse)
+{
+    if (B < 1 || K < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return -1;
+    const int G = Hq / Hkv;
+    int bad = 0;
+    long nrows = (long)B * Hq * K;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long row = 0; row < nrows; ++row) {
+        const int b = (int)(row / ((long)Hq * K));
+        const int h = (int)((row / K) % Hq);
+        const int i = (int)(row % K);
+        const int g = h / G;
+        const long L = lens[b];
+        const int nblk = (mask == O_BIDIR) ? K : i + 1;
+        const long n = L + nblk;
+        const double *qv = q + (((long)b * K + i) * Hq + h) * D;
+        double *s = (double *)malloc(sizeof(double) * (size_t)n);
+        const double **vrow = (const double **)malloc(sizeof(double *) * (size_t)n);
+        if (!s || !vrow) { bad = 1; free(s); free(vrow); continue; }
+        for (long t = 0; t < n; ++t) {
+            const double *kr, *vr;
+            if (t < L) {
+                kr = cache_row(k_cache, layout, cap, page_size, page_table,
+                               max_pages, num_pages, Hkv, D, b, g, t);
+                vr = cache_row(v_cache, layout, cap, page_size, page_table,
+                               max_pages, num_pages, Hkv, D, b, g, t);
+            } else {
+                long j = t - L;
+                kr = k_blk + (((long)b * K + j) * Hkv + g) * D;
+                vr = v_blk + (((long)b * K + j) * Hkv + g) * D;
+            }
+            if (!kr || !vr) { bad = 1; break; }
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d) dot += qv[d] * kr[d];
+            s[t] = scale * dot;
+            vrow[t] = vr;
+        }
+        if (!bad) {
+            double m = -INFINITY;
+            for (long t = 0; t < n; ++t) if (s[t] > m) m = s[t];
+            double denom = 0.0;
+            for (long t = 0; t < n; ++t) denom += exp(s[t] - m);
+            double *o = out + (((long)b * K + i) * Hq + h) * D;
+            for (int d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (long t = 0; t < n; ++t) acc += exp(s[t] - m) * vrow[t][d];
+                o[d] = acc / denom;
+            }
+            if (lse) lse[((long)b * Hq + h) * K + i] = m + log(denom);
+        }
+        free(s);
+        free(vrow);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Greedy prediction of one row: the smallest index v with x[v] >= x[u] for
+ * every u (numeric comparison, so -0.0 equals +0.0).  [SUM] §2.3 step 3: a
+ * candidate is judged against the frozen AR view's greedy choice; both views'
+ * candidates are row argmaxes of their logits.  Returns -1 if a row holds a
+ * NaN (no greedy choice is defined then).
+ */
+int oracle_argmax_rows(const double *x, long rows, long V, int32_t *idx)
+{
+    if (rows < 0 || V < 1) return -1;
+    for (long r = 0; r < rows; ++r) {
+        const double *row = x + r * V;
+        long best = 0;
+        for (long v = 0; v < V; ++v) {
+            if (isnan(row[v])) return -1;
+            if (row[v] > row[best]) best = v;
+        }
+        idx[r] = (int32_t)best;
+    }
+    return 0;
+}
+
+/*
+ * Exact left-to-right consensus.  [SUM] §2.3 step 3.
+ *
+ * Block row i of both views predicts the same position (the token after the
+ * i-th block input).  Scan i = 0, 1, ...: the first i with d[i] != a[i] is
+ * the divergence index j (K if none).  The tokens a[0..j-1] equal the
+ * accepted candidates d[0..j-1]; a[j] is the AR correction.  So the step
+ * emits n = min(j + 1, K) tokens a[0..n-1]; the last emitted token becomes
+ * the next block's anchor.  emit_off is the exclusive prefix sum of n over
+ * the batch (emit_off[B] = total) and emitted packs the tokens at those
+ * offsets.
+ */
+void oracle_consensus(const int32_t *d, const int32_t *a, int B, int K,
+                      int32_t *j_out, int32_t *n_out, int32_t *emit_off,
+                      int32_t *emitted, int32_t *next_anchor)
+{
+    int32_t off = 0;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *db = d + (long)b * K;
+        const int32_t *ab = a + (long)b * K;
+        int j = 0;
+        while (j < K && db[j] == ab[j]) ++j;      /* strict left-to-right */
+        int n = (j < K) ? j + 1 : K;
+        j_out[b] = j;
+        n_out[b] = n;
+        emit_off[b] = off;
+        for (int i = 0; i < n; ++i) emitted[off + i] = ab[i];
+        next_anchor[b] = ab[n - 1];
+        off += n;
+    }
+    emit_off[B] = off;
+}
+
+/*
+ * Commit: append the accepted positions' KV to the shared cache.  [SUM] §2.3
+ * step 3 (commit the agreed prefix) and [REP] (the accepted tokens' KV state
+ * is appended to the shared cache).
+ *
+ * The rows appended are the AR view's block rows 0..n[b]-1 (the anchor and
+ * the n-1 accepted inputs after it), written at cache positions lens[b]+i
+ * for every layer and KV head.  Every other cache byte is left unchanged;
+ * lens_out[b] = lens[b] + n[b].  Elements are copied as opaque bytes.
+ *
+ * k_cache/v_cache: per layer (stride cache_layer_stride elements) the cache
+ * layout of oracle_block_attn; k_blk/v_blk: per layer (stride
+ * blk_layer_stride) [B][K][Hkv][D].  Returns -1 on a bad argument, a page
+ * index out of range or a row beyond the capacity.
+ */
+int oracle_kv_append(unsigned char *k_cache, unsigned char *v_cache,
+                     int layout, long cap, int page_size,
+                     const int32_t *page_table, int max_pages, int num_pages,
+                     const int32_t *lens, const unsigned char *k_blk,
+                     const unsigned char *v_blk, const int32_t *n,
+                     int32_t *lens_out, int B, int K, int Hkv, int D,
+                     int elem_bytes, int layers, long cache_layer_stride,
+                     long blk_layer_stride)
+{
+    const long row_bytes = (long)D * elem_bytes;
+    for (int b = 0; b < B; ++b)
+        if (n[b] < 0 || n[b] > K) return -1;
+    for (int l = 0; l < layers; ++l) {
+        for (int b = 0; b < B; ++b) {
+            for (int i = 0; i < n[b]; ++i) {
+                long t = (long)lens[b] + i;
+                for (int g = 0; g < Hkv; ++g) {
+                    long dst;
+                    if (layout == O_CONTIGUOUS) {
+                        if (t >= cap) return -1;
+                        dst = ((long)b * Hkv + g) * cap + t;
+                    } else {
+                        long lp = t / page_size;
+                        if (lp >= max_pages) return -1;
+                        int32_t page = page_table[(long)b * max_pages + lp];
+                        if (page < 0 || page >= num_pages) return -1;
+                        dst = ((long)page * Hkv + g) * page_size + t % page_size;
+                    }
+                    long src = ((long)b * K + i) * Hkv + g;
+                    long cdst = (l * cache_layer_stride + dst * D) * elem_bytes;
+                    long csrc = (l * blk_layer_stride + src * D) * elem_bytes;
+                    memcpy(k_cache + cdst, k_blk + csrc, (size_t)row_bytes);
+                    memcpy(v_cache + cdst, v_blk + csrc, (size_t)row_bytes);
+                }
+            }
+        }
+    }
+    for (int b = 0; b < B; ++b) lens_out[b] = lens[b] + n[b];
+    return 0;
+}
+
+/* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

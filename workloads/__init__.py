@@ -1,0 +1,229 @@
+"""Seeded synthetic inputs for the Orthrus decode step.
+
+This module draws random numbers and lays them out; it performs none of the
+method's arithmetic (no attention, no consensus, no append).  Both the fp64
+oracle and the HIP path receive the tensors it returns, so neither side
+generates its own inputs.
+
+All draws use ``torch.Generator('cpu')``: fp32 N(0,1), rounded to the target
+dtype by round-to-nearest-even.  Seeds are ``1000 * config + tensor id (+ 16 *
+layer)`` so every tensor of every configuration is reproducible on any host.
+
+The five workloads are the Qwen3-shaped shapes the method is evaluated on
+(the summary's §4 names Qwen3 1.7B/4B/8B and a block of K=32; vocabulary
+151,936); their contents are synthetic, standing in for trained weights and
+the benchmark suites, which are not used.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+F32, BF16 = "f32", "bf16"
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
+
+# tensor ids used in seeds
+T_Q_DIFF, T_Q_AR, T_KC, T_VC, T_KB_DIFF, T_VB_DIFF, T_KB_AR, T_VB_AR = 1, 2, 3, 4, 5, 6, 7, 8
+T_LOGITS, T_LENS, T_PAGES, T_MATCHP = 9, 10, 11, 12
+
+
+@dataclass(frozen=True)
+class Config:
+    """Shape of one workload (one layer unless ``layers`` > 1)."""
+    cid: int
+    name: str
+    dtype: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    K: int
+    V: int
+    layers: int = 1
+    L: int = 0                       # fixed prefix length (contiguous)
+    L_range: tuple | None = None     # ragged prefix lengths (paged)
+    paged: bool = False
+    page_size: int = 16
+    p_match: float = 0.8
+    p_range: tuple | None = None     # per-request match probability range
+    num_splits: int = 0              # 0 = library's choice
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def scale(self) -> float:
+        return self.D ** -0.5
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DTYPE[self.dtype]
+
+    def with_(self, **kw) -> "Config":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Config(**d)
+
+
+CONFIGS = {
+    1: Config(1, "tiny-fp32", F32, B=1, Hq=2, Hkv=1, D=64, K=8, V=1000, L=128, p_match=0.8),
+    2: Config(2, "qwen3-1.7b-layer", BF16, B=1, Hq=16, Hkv=8, D=128, K=32, V=151936, L=2048,
+              p_match=0.8),
+    3: Config(3, "qwen3-8b-36layers", BF16, B=1, Hq=32, Hkv=8, D=128, K=32, V=151936, L=8192,
+              layers=36, p_match=0.85),
+    4: Config(4, "paged-serving-32req", BF16, B=32, Hq=32, Hkv=8, D=128, K=32, V=151936,
+              L_range=(512, 8192), paged=True, page_size=16, p_range=(0.5, 0.95)),
+    5: Config(5, "long-context-131k", BF16, B=1, Hq=32, Hkv=8, D=128, K=32, V=151936,
+              L=131072, p_match=0.8, num_splits=64),
+}
+LONG_CONTEXT_K_SWEEP = (4, 8, 16, 32, 64)
+
+
+def gen(seed: int) -> torch.Generator:
+    return torch.Generator().manual_seed(int(seed))
+
+
+def normal(shape, dtype, seed: int) -> torch.Tensor:
+    """N(0,1) drawn in fp32, rounded (RNE) to ``dtype``."""
+    x = torch.randn(tuple(shape), generator=gen(seed), dtype=torch.float32)
+    return x.to(dtype)
+
+
+def seed_of(cfg: Config, tensor_id: int, layer: int = 0, salt: int = 0) -> int:
+    return 1000 * cfg.cid + tensor_id + 16 * layer + 100000 * salt
+
+
+def prefix_lengths(cfg: Config, salt: int = 0) -> torch.Tensor:
+    """int32 [B] prefix lengths: fixed L, or uniform integers in L_range."""
+    if cfg.L_range is None:
+        return torch.full((cfg.B,), cfg.L, dtype=torch.int32)
+    lo, hi = cfg.L_range
+    return torch.randint(lo, hi + 1, (cfg.B,), generator=gen(seed_of(cfg, T_LENS, salt=salt)),
+                         dtype=torch.int32)
+
+
+def page_table(cfg: Config, lens: torch.Tensor, salt: int = 0):
+    """Random page table with room for the K appended rows of each request.
+
+    Request b owns ceil((lens[b] + K) / page_size) pages, taken from a random
+    permutation of all physical pages; unused entries are -1.
+    Returns (table int32 [B, max_pages], num_pages).
+    """
+    ps = cfg.page_size
+    need = [(int(l) + cfg.K + ps - 1) // ps for l in lens]
+    lmax = cfg.L_range[1] if cfg.L_range else int(lens.max())
+    max_pages = (lmax + cfg.K + ps - 1) // ps
+    num_pages = sum(need)
+    perm = torch.randperm(num_pages, generator=gen(seed_of(cfg, T_PAGES, salt=salt)))
+    table = torch.full((cfg.B, max_pages), -1, dtype=torch.int32)
+    pos = 0
+    for b, nb in enumerate(need):
+        table[b, :nb] = perm[pos:pos + nb].to(torch.int32)
+        pos += nb
+    return table, num_pages
+
+
+@dataclass
+class LayerInputs:
+    """One layer's attention inputs for both views (CPU tensors)."""
+    q_diff: torch.Tensor      # [B, K, Hq, D]
+    q_ar: torch.Tensor
+    k_cache: torch.Tensor     # [B, Hkv, cap, D] or [num_pages, Hkv, page, D]
+    v_cache: torch.Tensor
+    k_blk_diff: torch.Tensor  # [B, K, Hkv, D]  the diffusion module's own block K/V
+    v_blk_diff: torch.Tensor
+    k_blk_ar: torch.Tensor    # [B, K, Hkv, D]  the AR view's block K/V (appended)
+    v_blk_ar: torch.Tensor
+
+
+@dataclass
+class StepInputs:
+    cfg: Config
+    lens: torch.Tensor                 # int32 [B]
+    page_table: torch.Tensor | None    # int32 [B, max_pages]
+    num_pages: int
+    capacity: int                      # contiguous rows per (b, head)
+    layers: list                       # list[LayerInputs]
+    diff_logits: torch.Tensor          # [B, K, V]
+    ar_logits: torch.Tensor
+
+
+def layer_inputs(cfg: Config, layer: int, lens, num_pages: int, capacity: int,
+                 salt: int = 0) -> LayerInputs:
+    dt = cfg.torch_dtype
+    B, K, Hq, Hkv, D = cfg.B, cfg.K, cfg.Hq, cfg.Hkv, cfg.D
+    if cfg.paged:
+        cshape = (num_pages, Hkv, cfg.page_size, D)
+    else:
+        cshape = (B, Hkv, capacity, D)
+    s = lambda tid: seed_of(cfg, tid, layer, salt)  # noqa: E731
+    return LayerInputs(
+        q_diff=normal((B, K, Hq, D), dt, s(T_Q_DIFF)),
+        q_ar=normal((B, K, Hq, D), dt, s(T_Q_AR)),
+        k_cache=normal(cshape, dt, s(T_KC)),
+        v_cache=normal(cshape, dt, s(T_VC)),
+        k_blk_diff=normal((B, K, Hkv, D), dt, s(T_KB_DIFF)),
+        v_blk_diff=normal((B, K, Hkv, D), dt, s(T_VB_DIFF)),
+        k_blk_ar=normal((B, K, Hkv, D), dt, s(T_KB_AR)),
+        v_blk_ar=normal((B, K, Hkv, D), dt, s(T_VB_AR)),
+    )
+
+
+def consensus_logits(B: int, K: int, V: int, p, dtype, seed: int):
+    """AR logits N(0,1); diffusion logits a copy in which each position keeps
+    the AR argmax with probability p, and otherwise gets +10 (added in fp32,
+    rounded to dtype) on one uniformly chosen token other than the AR argmax.
+
+    ``p`` is a float or a length-B sequence (per-request probability).
+    Returns (diff_logits, ar_logits), both [B, K, V] in ``dtype``.
+    """
+    g = gen(seed)
+    ar = torch.randn((B, K, V), generator=g, dtype=torch.float32).to(dtype)
+    diff = ar.clone()
+    if isinstance(p, (list, tuple)):
+        pb = torch.tensor(p, dtype=torch.float64)
+    else:
+        pb = torch.full((B,), float(p), dtype=torch.float64)
+    coin = torch.rand((B, K), generator=g, dtype=torch.float64)
+    pick = torch.randint(0, max(V - 1, 1), (B, K), generator=g)
+    top = ar.float().argmax(dim=-1)           # input construction only
+    for b in range(B):
+        for i in range(K):
+            if coin[b, i] >= pb[b] and V > 1:
+                u = int(pick[b, i])
+                if u >= int(top[b, i]):
+                    u += 1
+                diff[b, i, u] = (ar[b, i, u].float() + 10.0).to(dtype)
+    return diff, ar
+
+
+def match_probabilities(cfg: Config, salt: int = 0):
+    if cfg.p_range is None:
+        return cfg.p_match
+    lo, hi = cfg.p_range
+    u = torch.rand((cfg.B,), generator=gen(seed_of(cfg, T_MATCHP, salt=salt)),
+                   dtype=torch.float64)
+    return (lo + (hi - lo) * u).tolist()
+
+
+def step_inputs(cfg: Config, layers: int | None = None, salt: int = 0,
+                with_logits: bool = True) -> StepInputs:
+    """All inputs of one decode step of ``cfg`` (CPU tensors)."""
+    nl = cfg.layers if layers is None else layers
+    lens = prefix_lengths(cfg, salt)
+    if cfg.paged:
+        table, num_pages = page_table(cfg, lens, salt)
+        capacity = 0
+    else:
+        table, num_pages = None, 0
+        capacity = int(lens.max()) + cfg.K
+    lay = [layer_inputs(cfg, l, lens, num_pages, capacity, salt) for l in range(nl)]
+    if with_logits:
+        diff, ar = consensus_logits(cfg.B, cfg.K, cfg.V, match_probabilities(cfg, salt),
+                                    cfg.torch_dtype, seed_of(cfg, T_LOGITS, salt=salt))
+    else:
+        diff = ar = None
+    return StepInputs(cfg, lens, table, num_pages, capacity, lay, diff, ar)

@@ -1,0 +1,110 @@
+// Commit of the accepted positions' KV into the shared cache, gfx950.
+//
+// Operation (Orthrus summary on gist.science, §2.3 step 3: commit the agreed
+// prefix; agents-report core design: the accepted tokens' KV state is
+// appended to the shared cache): for every layer, request b and i < n[b],
+// the AR view's block row i (all KV heads, K and V) is copied bit-exactly to
+// cache row lens[b] + i; lens_out[b] = lens[b] + n[b].
+//
+// Design: the accepted rows form a compacted list, indexed through the
+// exclusive prefix sum of n over the batch (recomputed in LDS by every
+// work-group: B is small next to the copy).  Each work-group copies a few
+// compacted rows of one layer with 16-byte loads/stores, so the grid work is
+// proportional to the accepted rows, not to B*K.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace orthrus {
+
+constexpr int kAppendRowsPerWG = 4;
+constexpr int kAppendMaxB = 8192;
+
+__global__ void __launch_bounds__(256) kv_append_kernel(AppendParams p, int chunks_per_layer)
+{
+    __shared__ int off[kAppendMaxB + 1];
+    __shared__ int part[256];
+    const int tid = threadIdx.x;
+    const int layer = blockIdx.x / chunks_per_layer;
+    const int chunk = blockIdx.x % chunks_per_layer;
+
+    // exclusive prefix sum of n over the batch (contiguous runs per thread)
+    const int per = (p.B + 255) / 256;
+    const int b0 = tid * per;
+    const int b1 = (b0 + per < p.B) ? b0 + per : p.B;
+    int local = 0;
+    for (int b = b0; b < b1; ++b) {
+        int n = p.n_emit[b];
+        n = n < 0 ? 0 : (n > p.K ? p.K : n);
+        off[b] = n;          // temporarily the count
+        local += n;
+    }
+    part[tid] = local;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        const int v = tid >= o ? part[tid - o] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int run = part[tid] - local;
+    for (int b = b0; b < b1; ++b) {
+        const int n = off[b];
+        off[b] = run;
+        run += n;
+    }
+    if (tid == 255) off[p.B] = part[255];
+    __syncthreads();
+    if (layer == 0 && chunk == 0) {
+        for (int b = tid; b < p.B; b += 256) p.lens_out[b] = p.lens[b] + (off[b + 1] - off[b]);
+    }
+
+    const int total = off[p.B];
+    const int gpr = p.D * p.esize / 16;             // 16-byte granules per head row
+    const int per_row = 2 * p.Hkv * gpr;            // K and V granules of one block row
+    const char *kb = (const char *)p.kb + (int64_t)layer * p.blk_layer_stride * p.esize;
+    const char *vb = (const char *)p.vb + (int64_t)layer * p.blk_layer_stride * p.esize;
+    char *kc = (char *)p.kc + (int64_t)layer * p.cache_layer_stride * p.esize;
+    char *vc = (char *)p.vc + (int64_t)layer * p.cache_layer_stride * p.esize;
+    const int64_t row_bytes = (int64_t)p.D * p.esize;
+
+    for (int rr = 0; rr < kAppendRowsPerWG; ++rr) {
+        const int cidx = chunk * kAppendRowsPerWG + rr;
+        if (cidx >= total) break;
+        // request owning compacted row cidx: last b with off[b] <= cidx
+        int lo = 0, hi = p.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off[mid] <= cidx) lo = mid;
+            else hi = mid - 1;
+        }
+        const int b = lo;
+        const int i = cidx - off[b];
+        const int64_t t = (int64_t)p.lens[b] + i;
+        for (int x = tid; x < per_row; x += 256) {
+            const bool isv = x >= p.Hkv * gpr;
+            const int y = isv ? x - p.Hkv * gpr : x;
+            const int g = y / gpr;
+            const int q = y % gpr;
+            int64_t dst_row;
+            if (p.layout == 0) {
+                dst_row = ((int64_t)b * p.Hkv + g) * p.cap + t;
+            } else {
+                const int page = p.page_table[(int64_t)b * p.maxp + (t >> 4)];
+                dst_row = ((int64_t)page * p.Hkv + g) * 16 + (t & 15);
+            }
+            const int64_t src_row = ((int64_t)b * p.K + i) * p.Hkv + g;
+            const u32x4 v = *(const u32x4 *)((isv ? vb : kb) + src_row * row_bytes + q * 16);
+            *(u32x4 *)((isv ? vc : kc) + dst_row * row_bytes + q * 16) = v;
+        }
+    }
+}
+
+hipError_t launch_kv_append(const AppendParams &p, hipStream_t st)
+{
+    const int chunks = (p.B * p.K + kAppendRowsPerWG - 1) / kAppendRowsPerWG;
+    hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)(chunks * p.layers)), dim3(256), 0, st, p,
+                       chunks);
+    return hipGetLastError();
+}
+
+}  // namespace orthrus

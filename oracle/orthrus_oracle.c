@@ -109,11 +109,14 @@ int oracle_block_attn(const double *q, const double *k_cache,
             double m = -INFINITY;
             for (long t = 0; t < n; ++t) if (s[t] > m) m = s[t];
             double denom = 0.0;
-            for (long t = 0; t < n; ++t) denom += exp(s[t] - m);
+            for (long t = 0; t < n; ++t) {
+                s[t] = exp(s[t] - m);            /* s now holds the weight w_t */
+                denom += s[t];
+            }
             double *o = out + (((long)b * K + i) * Hq + h) * D;
             for (int d = 0; d < D; ++d) {
                 double acc = 0.0;
-                for (long t = 0; t < n; ++t) acc += exp(s[t] - m) * vrow[t][d];
+                for (long t = 0; t < n; ++t) acc += s[t] * vrow[t][d];
                 o[d] = acc / denom;
             }
             if (lse) lse[((long)b * Hq + h) * K + i] = m + log(denom);

@@ -1,0 +1,138 @@
+"""The C ABI on the host (CPU only): the library loads, exports every function
+include/orthrus.h declares, and rejects every invalid argument with its
+status code before touching a device (no call here reaches a launch)."""
+import ctypes
+
+import pytest
+
+from ar_shared_kv_amd import _binding as B
+
+FAKE = 1 << 20           # a non-null, 16-byte-aligned stand-in address (never dereferenced)
+
+
+def cache(layout=B.CONTIGUOUS, capacity=8224, max_len=8192, pages=0, maxp=0, page_size=16):
+    c = B.orthrus_cache()
+    c.layout, c.capacity, c.max_len = layout, capacity, max_len
+    c.k = c.v = c.lens = FAKE
+    c.page_size = page_size
+    if layout == B.PAGED:
+        c.page_table, c.num_pages, c.max_pages_per_req, c.capacity = FAKE, pages, maxp, 0
+    return c
+
+
+def attn(c, **kw):
+    a = dict(q=FAKE, kb=FAKE, vb=FAKE, out=FAKE, lse=None, B=1, K=32, Hq=32, Hkv=8, D=128,
+             dtype=B.BF16, mask=B.CAUSAL, scale=0.088, splits=0, ws=None, wsb=0)
+    a.update(kw)
+    return B.lib().orthrus_block_attn(ctypes.byref(c) if c is not None else None, a["q"], a["kb"],
+                                      a["vb"], a["out"], a["lse"], a["B"], a["K"], a["Hq"],
+                                      a["Hkv"], a["D"], a["dtype"], a["mask"], a["scale"],
+                                      a["splits"], a["ws"], a["wsb"], None)
+
+
+def test_exports_every_declared_function():
+    declared = B.header_functions()
+    assert len(declared) == 9
+    for name in declared:
+        assert hasattr(B.lib(), name), name
+    assert set(declared) == set(B.SIGNATURES)
+
+
+def test_status_strings_complete():
+    names = [B.status_string(s) for s in range(7)]
+    assert len(set(names)) == 7 and "unknown" not in " ".join(names)
+    assert B.status_string(99) == "unknown status"
+    assert B.orthrus_version() == 10000
+
+
+def test_block_attn_validation_codes():
+    c = cache()
+    assert attn(None) == B.ERR_NULL
+    assert attn(c, q=None) == B.ERR_NULL
+    assert attn(c, out=None) == B.ERR_NULL
+    assert attn(c, B=0) == B.ERR_SHAPE
+    assert attn(c, Hq=30) == B.ERR_SHAPE            # Hq % Hkv != 0
+    assert attn(c, K=0) == B.ERR_SHAPE
+    assert attn(c, scale=float("nan")) == B.ERR_SHAPE
+    assert attn(c, K=65) == B.ERR_UNSUPPORTED
+    assert attn(c, D=96) == B.ERR_UNSUPPORTED
+    assert attn(c, Hq=8 * 17) == B.ERR_UNSUPPORTED  # G = 17 > 16
+    assert attn(c, dtype=2) == B.ERR_DTYPE
+    assert attn(c, mask=3) == B.ERR_DTYPE
+    assert attn(c, q=FAKE + 2) == B.ERR_UNSUPPORTED  # misaligned
+    assert attn(cache(layout=7)) == B.ERR_DTYPE
+    assert attn(cache(max_len=9000)) == B.ERR_SHAPE  # hint beyond capacity
+    # split-KV needs a workspace
+    need = B.orthrus_block_attn_workspace_bytes(c, 1, 32, 32, 8, 128, B.BF16, 0)
+    assert need > 0
+    assert attn(c) == B.ERR_WORKSPACE
+    assert attn(c, ws=FAKE, wsb=need - 1) == B.ERR_WORKSPACE
+    pc = cache(layout=B.PAGED, pages=100, maxp=10, max_len=0, page_size=8)
+    assert attn(pc) == B.ERR_UNSUPPORTED            # page size must be 16
+    pc = cache(layout=B.PAGED, pages=100, maxp=10, max_len=0)
+    pc.page_table = None
+    assert attn(pc) == B.ERR_NULL
+
+
+def test_block_attn_workspace_formula():
+    c = cache(capacity=131136, max_len=131072)
+    # 64 splits of 2048 keys: partials [B*Hkv][S][M][D] + lse [B*Hkv][S][M], fp32
+    n = B.orthrus_block_attn_workspace_bytes(c, 1, 64, 32, 8, 128, B.BF16, 64)
+    assert n == 1 * 8 * 64 * 256 * 129 * 4
+    # one split -> no workspace
+    small = cache(capacity=128, max_len=128)
+    assert B.orthrus_block_attn_workspace_bytes(small, 1, 8, 2, 1, 64, B.F32, 0) == 0
+    assert B.orthrus_block_attn_workspace_bytes(c, 1, 64, 32, 8, 96, B.BF16, 0) == 0   # invalid
+
+
+def test_consensus_validation_and_workspace():
+    f = B.lib().orthrus_consensus
+    args = [FAKE, FAKE, 1, 32, 151936, B.BF16] + [FAKE] * 7
+    need = B.orthrus_consensus_workspace_bytes(1, 32, 151936, B.BF16)
+    chunks = -(-151936 * 2 // 16384)
+    assert need == 2 * 32 * chunks * 8
+    assert f(*args, FAKE, need - 8, None) == B.ERR_WORKSPACE
+    assert f(*args, None, need, None) == B.ERR_WORKSPACE
+    bad = list(args)
+    bad[0] = None
+    assert f(*bad, FAKE, need, None) == B.ERR_NULL
+    bad = list(args)
+    bad[5] = 9
+    assert f(*bad, FAKE, need, None) == B.ERR_DTYPE
+    bad = list(args)
+    bad[3] = 65
+    assert f(*bad, FAKE, need, None) == B.ERR_UNSUPPORTED
+    bad = list(args)
+    bad[4] = 0
+    assert f(*bad, FAKE, need, None) == B.ERR_SHAPE
+    assert B.orthrus_argmax_workspace_bytes(10, 1000, B.F32) == 10 * 1 * 8
+    assert B.lib().orthrus_argmax(FAKE, 0, 10, B.F32, FAKE, FAKE, 8, None) == B.ERR_SHAPE
+
+
+def test_kv_append_validation():
+    c = cache(capacity=100, max_len=0)
+    f = B.lib().orthrus_kv_append
+    base = [FAKE, FAKE, FAKE, FAKE + 4096, 1, 32, 8, 128, B.BF16, 1, 0, 0, None]
+    b = list(base)
+    b[3] = FAKE    # lens_out aliases cache.lens
+    assert f(ctypes.byref(c), *b) == B.ERR_SHAPE
+    b = list(base)
+    b[2] = None
+    assert f(ctypes.byref(c), *b) == B.ERR_NULL
+    b = list(base)
+    b[7] = 80
+    assert f(ctypes.byref(c), *b) == B.ERR_UNSUPPORTED
+    b = list(base)
+    b[9] = 0
+    assert f(ctypes.byref(c), *b) == B.ERR_SHAPE
+    b = list(base)
+    b[9], b[10] = 2, 3        # layer stride not a multiple of 16 bytes
+    assert f(ctypes.byref(c), *b) == B.ERR_UNSUPPORTED
+
+
+def test_single_hip_runtime_in_process():
+    import torch  # noqa: F401
+    B.lib()
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths

@@ -227,3 +227,26 @@ def step_inputs(cfg: Config, layers: int | None = None, salt: int = 0,
     else:
         diff = ar = None
     return StepInputs(cfg, lens, table, num_pages, capacity, lay, diff, ar)
+
+
+def custom_step(B: int, Hq: int, Hkv: int, D: int, K: int, lens, dtype=BF16, paged=False,
+                seed: int = 0, V: int = 1000, p=0.8, extra_capacity: int = 0) -> StepInputs:
+    """A small step with explicit per-request prefix lengths (edge cases).
+
+    Contiguous caches get capacity max(lens) + K + extra_capacity; paged ones
+    a random page table with room for the K appended rows.
+    """
+    lens_t = torch.tensor(list(lens), dtype=torch.int32)
+    assert lens_t.numel() == B
+    cfg = Config(90 + (seed % 10), f"custom-{seed}", dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, K=K, V=V,
+                 L_range=(int(lens_t.min()), int(lens_t.max())), paged=paged, p_match=p)
+    salt = 1 + seed
+    if paged:
+        table, num_pages = page_table(cfg, lens_t, salt)
+        capacity = 0
+    else:
+        table, num_pages = None, 0
+        capacity = int(lens_t.max()) + K + extra_capacity
+    lay = [layer_inputs(cfg, 0, lens_t, num_pages, capacity, salt)]
+    diff, ar = consensus_logits(B, K, V, p, cfg.torch_dtype, seed_of(cfg, T_LOGITS, salt=salt))
+    return StepInputs(cfg, lens_t, table, num_pages, capacity, lay, diff, ar)

@@ -23,8 +23,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct AttnPlan {
     int status;
-    int M, G, rows_per_wg, row_blocks, SL, S_grid;
-    size_t ws_bytes;
+    int M, G, rows_per_wg, row_blocks, SL, S_grid, ds;
+    size_t ws_bytes, ws_lse_offset;
 };
 
 // Shape/dtype checks shared by the workspace query and the launch.
@@ -62,11 +62,16 @@ AttnPlan plan_block_attn(const orthrus_cache *c, int B, int K, int Hq, int Hkv, 
     pl.M = pl.G * K;
     pl.rows_per_wg = attn_rows_per_wg(dtype, pl.M);
     pl.row_blocks = (int)ceil_div(pl.M, pl.rows_per_wg);
+    // Output-column split: with bf16, D = 128 and 128 query rows per work-group,
+    // two work-groups share a key range (each loads K, and half of V), which
+    // halves the number of key splits, and so the split partials, for the same
+    // number of work-groups.  Only with the automatic split plan.
+    pl.ds = 1;
     int64_t S;
     if (num_splits > 0) {
         S = num_splits;
     } else {
-        S = ceil_div(kTargetWorkGroups, (int64_t)B * Hkv * pl.row_blocks);
+        S = ceil_div(kTargetWorkGroups, (int64_t)B * Hkv * pl.row_blocks * pl.ds);
         const int64_t cap_s = ceil_div(lmax, kMinKeysPerSplit);
         if (S > cap_s) S = cap_s;
     }
@@ -83,13 +88,18 @@ AttnPlan plan_block_attn(const orthrus_cache *c, int B, int K, int Hq, int Hkv, 
         S_grid = ceil_div(c->max_pages_per_req * (int64_t)c->page_size, SL);
     }
     if (S_grid < 1) S_grid = 1;
-    if ((int64_t)B * Hkv * S_grid > kMaxGrid || pl.row_blocks > 65535) {
+    if ((int64_t)B * Hkv * S_grid > kMaxGrid || (int64_t)pl.row_blocks * pl.ds > 65535) {
         pl.status = ORTHRUS_ERR_UNSUPPORTED;
         return pl;
     }
     pl.SL = (int)SL;
     pl.S_grid = (int)S_grid;
-    pl.ws_bytes = S_grid > 1 ? (size_t)B * Hkv * S_grid * pl.M * (size_t)(D + 1) * sizeof(float) : 0;
+    // partials in the path's dtype (bf16 or fp32), then the fp32 base-2 lse
+    const size_t esz = dtype == ORTHRUS_BF16 ? 2 : 4;
+    const size_t mpad = (size_t)(pl.M + 31) / 32 * 32;
+    const size_t rows = (size_t)B * Hkv * S_grid * mpad;
+    pl.ws_lse_offset = ((size_t)B * Hkv * S_grid * mpad * D * esz + 255) / 256 * 256;
+    pl.ws_bytes = S_grid > 1 ? pl.ws_lse_offset + rows * sizeof(float) : 0;
     pl.status = ORTHRUS_OK;
     return pl;
 }
@@ -162,6 +172,7 @@ int orthrus_block_attn(const orthrus_cache *cache, const void *q, const void *k_
     p.Hkv = Hkv;
     p.G = pl.G;
     p.M = pl.M;
+    p.Mpad = (pl.M + 31) / 32 * 32;
     p.D = D;
     p.cap = cache->capacity;
     p.maxp = cache->max_pages_per_req;
@@ -171,10 +182,11 @@ int orthrus_block_attn(const orthrus_cache *cache, const void *q, const void *k_
     p.S_grid = pl.S_grid;
     p.rows_per_wg = pl.rows_per_wg;
     p.row_blocks = pl.row_blocks;
+    p.ds = pl.ds;
     p.c = scale * 1.4426950408889634f;
     if (pl.S_grid > 1) {
-        p.ws_o = static_cast<float *>(workspace);
-        p.ws_lse = p.ws_o + (size_t)B * Hkv * pl.S_grid * pl.M * D;
+        p.ws_o = workspace;
+        p.ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.ws_lse_offset);
     }
     return map_err(launch_block_attn(p, dtype, stream));
 }

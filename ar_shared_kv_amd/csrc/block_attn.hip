@@ -47,37 +47,60 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, uint32_t lds_addr) {
 
 }  // namespace
 
+// Element offset of (row r, column d) inside one split partial block of
+// Mpad x D values, in the order the MFMA accumulators hold them: every store
+// of four columns by a wave covers 512 contiguous bytes (bf16).
+__device__ __forceinline__ int64_t frag_offset(int r, int d, int D) {
+    return (((((int64_t)(r >> 5) * (D >> 5) + (d >> 5)) * 4 + ((d & 31) >> 3)) * 2 + ((d & 7) >> 2)) * 32
+            + (r & 31)) * 4 + (d & 3);
+}
+
 // --------------------------------------------------------------------------
 // bf16 MFMA kernel
 // --------------------------------------------------------------------------
 // NR: 32-row query groups per work-group; KS: waves sharing one row group,
-// each taking a 64/KS-key slice of every tile.  Waves = NR*KS.
-template <int D, int NR, int KS, int NSTAGE, bool PAGED>
+// each taking a 64/KS-key slice of every tile (waves = NR*KS); DS: the output
+// columns are split over DS work-groups (each loads all of K for the scores
+// but only its D/DS columns of V); NSTAGE: ring slots; NPRE: tiles kept in
+// flight ahead of the one being computed; QLDS: the query tile is fetched by
+// LDS DMA as part of the prologue instead of through VGPR loads.
+template <int D, int NR, int KS, int DS, int NSTAGE, int NPRE, bool PAGED, bool QLDS>
 __global__ void __launch_bounds__(64 * NR * KS)
 attn_bf16_kernel(AttnParams p)
 {
     constexpr int NW = NR * KS;
-    constexpr int GPR = D / 8;                 // 16-byte granules per row
-    constexpr int RPC = 64 / GPR;              // rows per 1 KiB chunk
-    constexpr int CPT = TK / RPC;              // chunks per K (or V) tile
-    constexpr int TILE_ELEMS = TK * D;         // per K or V tile
-    constexpr int TILE_BYTES = TILE_ELEMS * 2;
+    constexpr int DC = D / DS;                 // output columns of this work-group
+    constexpr int GPR = D / 8;                 // 16-byte granules per K row
+    constexpr int GPRV = DC / 8;               // 16-byte granules per V row slice
+    constexpr int RPCK = 64 / GPR;             // K rows per 1 KiB chunk
+    constexpr int RPCV = 64 / GPRV;            // V rows per 1 KiB chunk
+    constexpr int CK = TK / RPCK;              // K chunks per tile
+    constexpr int CV = TK / RPCV;              // V chunks per tile
+    constexpr int K_BYTES = TK * D * 2;
+    constexpr int V_BYTES = TK * DC * 2;
+    constexpr int SLOT = K_BYTES + V_BYTES;
     constexpr int KPW = TK / KS;               // keys per wave per tile
     constexpr int NBLK = KPW / 32;             // S^T 32x32 blocks per wave
-    constexpr int NDT = D / 32;                // O^T tiles
+    constexpr int NDT = DC / 32;               // O^T tiles
+    constexpr int QROWS = 32 * NR;
+    constexpr int Q_BYTES = QLDS ? QROWS * D * 2 : 0;
+    constexpr int CQ = Q_BYTES / 1024;         // query chunks
     static_assert(KPW % 32 == 0, "each wave needs whole 32-key blocks");
-    static_assert((2 * CPT) % NW == 0, "chunks must split evenly over waves");
-    constexpr int LPT = 2 * CPT / NW;          // loads per tile per lane
-    constexpr int HALF = LPT / 2;              // loads [0,HALF) K, [HALF,LPT) V
+    static_assert(CK % NW == 0 && CV % NW == 0 && CQ % NW == 0, "chunks must split evenly");
+    static_assert(NPRE >= 1 && NPRE < NSTAGE, "prefetch depth");
+    constexpr int LK = CK / NW, LV = CV / NW, LQ = CQ / NW;
+    constexpr int LPT = LK + LV;               // DMA loads per tile per lane
+    static_assert(LPT * (NPRE + 1) + LQ <= 63, "vmcnt range");
     // Lazy rescaling: the running max only moves when a tile's max exceeds
     // it by more than 2^kLazy in exp2 units (weights stay <= 2^kLazy).
     constexpr float kLazy = 8.0f;
 
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[NSTAGE][2][TILE_ELEMS];
-    __shared__ int s_pages[PAGED ? kMaxSplitPages : 1];
+    constexpr int PAGE_BYTES = PAGED ? kMaxSplitPages * 4 : 0;
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * SLOT + Q_BYTES + PAGE_BYTES];
+    int* s_pages = reinterpret_cast<int*>(smem + NSTAGE * SLOT + Q_BYTES);   // PAGED only
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int rg = wave % NR;      // row group
     const int kg = wave / NR;      // key slice
@@ -86,36 +109,35 @@ attn_bf16_kernel(AttnParams p)
     const int s = blockIdx.x / BH;
     const int b = bh / p.Hkv;
     const int g = bh % p.Hkv;
-
-    // ---- key range of this split (same rule as attn_merge_kernel) ----
-    const int L = p.lens[b];
-    int S_b = (L + p.SL - 1) / p.SL;
-    S_b = S_b < 1 ? 1 : (S_b > p.S_grid ? p.S_grid : S_b);
-    if (s >= S_b) return;
-    const bool last = (s == S_b - 1);
+    const int rb = blockIdx.y / DS;   // row block
+    const int dh = blockIdx.y % DS;   // column slice
+    const int col0 = dh * DC;
     const int kbeg = s * p.SL;
-    const int kend = last ? L : kbeg + p.SL;
-    const int n_cache_tiles = (kend - kbeg + TK - 1) / TK;
-    const int n_tiles = n_cache_tiles + (last ? 1 : 0);   // K <= 64 = TK
 
-    // ---- page ids of this split (paged layout) ----
-    if constexpr (PAGED) {
-        const int pg0 = kbeg / 16;
-        const int npg = (kend - kbeg + 15) / 16;
-        for (int i = tid; i < npg; i += 64 * NW)
-            s_pages[i] = p.page_table[(int64_t)b * p.maxp + pg0 + i];
-        __syncthreads();
-    }
-
-    // ---- query rows of this lane: B operand Q^T[d][q], q = lane % 32 ----
+    // ---- query rows: lane column q = lane % 32 of row group rg ----
     const int half = lane >> 5;
-    const int r = blockIdx.y * (32 * NR) + rg * 32 + (lane & 31);
+    const int r = rb * QROWS + rg * 32 + (lane & 31);
     const bool row_ok = r < p.M;
     const int hl = row_ok ? r / p.K : 0;
     const int qi = row_ok ? r % p.K : 0;
     const int h = g * p.G + hl;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(ORTHRUS_LDS void*)&smem[0];
+    const uint32_t q_lds = lds_base + NSTAGE * SLOT;
     bf16x8 qreg[D / 16];
-    {
+    if constexpr (QLDS) {
+        // DMA the query tile (rows XOR-swizzled like K) ahead of the K/V ring
+#pragma unroll
+        for (int i = 0; i < LQ; ++i) {
+            const int cc = i * NW + wave;
+            const int row = cc * RPCK + lane / GPR;
+            const int rr = rb * QROWS + row;
+            const int rq = rr < p.M ? rr : 0;
+            const int gr = (lane % GPR) ^ (row & (GPR - 1));
+            const char* src = (const char*)p.q +
+                ((((int64_t)b * p.K + rq % p.K) * p.Hq + g * p.G + rq / p.K) * D + gr * 8) * 2;
+            lds_dma16(src, q_lds + cc * 1024);
+        }
+    } else {
         const uint16_t* qp = (const uint16_t*)p.q + (((int64_t)b * p.K + qi) * p.Hq + h) * D
                              + 8 * half;
 #pragma unroll
@@ -138,55 +160,57 @@ attn_bf16_kernel(AttnParams p)
     const int64_t cont_base = ((int64_t)b * p.Hkv + g) * p.cap * D * 2;    // bytes
     const int64_t blk_base = ((int64_t)b * p.K * p.Hkv + g) * D * 2;
     const int blk_stride = p.Hkv * D * 2;
-    const int prow = lane / GPR;
-    const int pgr = lane % GPR;
     int lrow[LPT];                 // tile row loaded by this lane for load i
-    uint32_t lgoff[LPT];           // swizzled granule byte offset within the row
+    uint32_t loff[LPT];            // byte offset of the (swizzled) granule in the row
+    uint32_t ldst[LPT];            // LDS byte offset of the chunk within a slot
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-        const bool isv = i >= HALF;
-        const int cc = (isv ? i - HALF : i) * NW + wave;
-        lrow[i] = cc * RPC + prow;
-        lgoff[i] = 16u * (uint32_t)(isv ? (pgr ^ (2 * (lrow[i] & 3))) : (pgr ^ (lrow[i] & (GPR - 1))));
+        const bool isv = i >= LK;
+        const int cc = (isv ? i - LK : i) * NW + wave;
+        if (!isv) {
+            lrow[i] = cc * RPCK + lane / GPR;
+            loff[i] = 16u * (uint32_t)((lane % GPR) ^ (lrow[i] & (GPR - 1)));
+            ldst[i] = cc * 1024;
+        } else {
+            lrow[i] = cc * RPCV + lane / GPRV;
+            loff[i] = 2u * col0 + 16u * (uint32_t)((lane % GPRV) ^ (2 * (lrow[i] & 3)));
+            ldst[i] = K_BYTES + cc * 1024;
+        }
     }
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(ORTHRUS_LDS void*)&smem[0][0][0];
 
-    // issue the global->LDS loads of tile t into ring slot t % NSTAGE
-    auto issue = [&](int t) {
-        const uint32_t slot_lds = lds_base + (uint32_t)((t % NSTAGE) * 2 * TILE_BYTES);
-        const bool is_blk = t >= n_cache_tiles;
-        const int start = is_blk ? 0 : kbeg + t * TK;
-        const int count = is_blk ? p.K : (kend - start < TK ? kend - start : TK);
+    // Key range of this split: needs lens[b], which is read after the first
+    // loads are in flight (contiguous layout: the split's nominal tiles are
+    // fetched speculatively, rows clamped to the capacity).
+    int kend = kbeg + p.SL;
+    int n_cache_tiles = 0;
+    int last_issued = -1;      // highest tile index of the true sequence issued so far
+
+    // issue the global->LDS loads of tile t (rows start..start+count-1 of the
+    // cache, or the block rows) into ring slot t % NSTAGE
+    auto issue_rows = [&](int t, bool is_blk, int start, int count) {
+        const uint32_t slot_lds = lds_base + (uint32_t)((t % NSTAGE) * SLOT);
         if (!is_blk && !PAGED && count == TK) {
             // fast path: a full contiguous tile, rows D*2 bytes apart
             const char* kt = kc + cont_base + (int64_t)start * D * 2;
             const char* vt = vc + cont_base + (int64_t)start * D * 2;
 #pragma unroll
-            for (int i = 0; i < LPT; ++i) {
-                const bool isv = i >= HALF;
-                const int cc = (isv ? i - HALF : i) * NW + wave;
-                lds_dma16((isv ? vt : kt) + (uint32_t)(lrow[i] * D * 2) + lgoff[i],
-                          slot_lds + (isv ? TILE_BYTES : 0) + cc * 1024);
-            }
+            for (int i = 0; i < LPT; ++i)
+                lds_dma16((i >= LK ? vt : kt) + (uint32_t)(lrow[i] * D * 2) + loff[i],
+                          slot_lds + ldst[i]);
         } else if (!is_blk && PAGED && count == TK) {
             // full paged tile: 4 pages of 16 rows
             const int pidx = (start - kbeg) >> 4;
 #pragma unroll
             for (int i = 0; i < LPT; ++i) {
-                const bool isv = i >= HALF;
-                const int cc = (isv ? i - HALF : i) * NW + wave;
                 const int page = s_pages[pidx + (lrow[i] >> 4)];
-                const char* base = (isv ? vc : kc) +
-                    ((int64_t)page * p.Hkv + g) * (16 * D * 2);
-                lds_dma16(base + (uint32_t)((lrow[i] & 15) * D * 2) + lgoff[i],
-                          slot_lds + (isv ? TILE_BYTES : 0) + cc * 1024);
+                const char* base = (i >= LK ? vc : kc) + ((int64_t)page * p.Hkv + g) * (16 * D * 2);
+                lds_dma16(base + (uint32_t)((lrow[i] & 15) * D * 2) + loff[i], slot_lds + ldst[i]);
             }
         } else {
             // partial cache tile or the block tile: clamp rows to count-1
 #pragma unroll
             for (int i = 0; i < LPT; ++i) {
-                const bool isv = i >= HALF;
-                const int cc = (isv ? i - HALF : i) * NW + wave;
+                const bool isv = i >= LK;
                 const int rowc = lrow[i] < count ? lrow[i] : count - 1;
                 const char* src;
                 if (is_blk) {
@@ -199,42 +223,84 @@ attn_bf16_kernel(AttnParams p)
                 } else {
                     src = (isv ? vc : kc) + cont_base + (int64_t)(start + rowc) * D * 2;
                 }
-                lds_dma16(src + lgoff[i], slot_lds + (isv ? TILE_BYTES : 0) + cc * 1024);
+                lds_dma16(src + loff[i], slot_lds + ldst[i]);
             }
         }
     };
+    auto issue = [&](int t) {
+        const bool is_blk = t >= n_cache_tiles;
+        const int start = is_blk ? 0 : kbeg + t * TK;
+        const int count = is_blk ? p.K : (kend - start < TK ? kend - start : TK);
+        issue_rows(t, is_blk, start, count);
+        last_issued = t > last_issued ? t : last_issued;
+    };
+
+    // wait until at most `pending` later tiles of this lane are in flight
+    auto wait_tiles = [&](int pending) {
+        switch (pending) {
+            case 0: __builtin_amdgcn_s_waitcnt(vmcnt_encode(0)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(vmcnt_encode(LPT)); break;
+            case 2: __builtin_amdgcn_s_waitcnt(vmcnt_encode(2 * LPT)); break;
+            case 3: __builtin_amdgcn_s_waitcnt(vmcnt_encode(3 * LPT)); break;
+            default: __builtin_amdgcn_s_waitcnt(vmcnt_encode(4 * LPT)); break;
+        }
+    };
+    static_assert(NPRE <= 4, "wait_tiles covers up to 4 pending tiles");
+
+    // ---- prologue: NPRE tiles in flight; iteration t issues tile t + NPRE
+    // into the slot of an already consumed tile (NPRE < NSTAGE) ----
+    int spec = 0;   // speculative cache tiles issued before lens[b] is known
+    if constexpr (!PAGED) {
+        const int64_t nominal_end = (int64_t)kbeg + p.SL < p.cap ? (int64_t)kbeg + p.SL : p.cap;
+        const int nom = nominal_end > kbeg ? (int)((nominal_end - kbeg + TK - 1) / TK) : 0;
+        spec = nom < NPRE ? nom : NPRE;
+        for (int t = 0; t < spec; ++t) {
+            const int start = kbeg + t * TK;
+            const int64_t inb = p.cap - start;     // in-bounds rows of this tile
+            issue_rows(t, false, start, inb < TK ? (int)inb : TK);
+        }
+    }
+    // lens[b] through the scalar unit: a vector load would only return after
+    // every DMA issued above (vector loads complete in order)
+    const int L = ((const __attribute__((address_space(4))) int32_t*)p.lens)[b];
+    int S_b = (L + p.SL - 1) / p.SL;
+    S_b = S_b < 1 ? 1 : (S_b > p.S_grid ? p.S_grid : S_b);
+    if (s >= S_b) {                       // no keys for this split: drain the DMA, exit
+        __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));
+        return;
+    }
+    const bool last = (s == S_b - 1);
+    kend = last ? L : kbeg + p.SL;
+    n_cache_tiles = (kend - kbeg + TK - 1) / TK;
+    const int n_tiles = n_cache_tiles + (last ? 1 : 0);   // K <= 64 = TK
+    if (spec > n_cache_tiles) {
+        // a short last split: speculative tiles past its end are discarded;
+        // drain them before their slots take the block tile
+        __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));
+        spec = n_cache_tiles;
+    }
+    last_issued = spec - 1;
+    if constexpr (PAGED) {   // page ids of this split
+        const int pg0 = kbeg / 16;
+        const int npg = (kend - kbeg + 15) / 16;
+        for (int i = tid; i < npg; i += 64 * NW)
+            s_pages[i] = p.page_table[(int64_t)b * p.maxp + pg0 + i];
+        __syncthreads();
+    }
+    for (int t = spec; t < NPRE && t < n_tiles; ++t) issue(t);
 
     f32x16 oacc[NDT];
 #pragma unroll
     for (int i = 0; i < NDT; ++i) oacc[i] = f32x16{};
+    f32x16 lacc = f32x16{};    // row sums of the bf16 weights (ones x P^T on the MFMA)
     float m_run = -INFINITY;   // running max of raw scores (this lane's query)
-    float l_run = 0.f;         // running sum of this lane-half's weights
     const float c = p.c;       // scale * log2(e)
     const float lazy_raw = kLazy / c;
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
-    // prologue
-#pragma unroll
-    for (int t = 0; t < NSTAGE - 1; ++t)
-        if (t < n_tiles) issue(t);
-
-    for (int t = 0; t < n_tiles; ++t) {
-        // wait for this lane's loads of tile t, then make everyone's visible
-        if (t + NSTAGE - 2 < n_tiles)
-            __builtin_amdgcn_s_waitcnt(vmcnt_encode((NSTAGE - 2) * LPT));
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));
-        __syncthreads();
-        if (t + NSTAGE - 1 < n_tiles) issue(t + NSTAGE - 1);
-
-        const int slot = t % NSTAGE;
-        const uint16_t* Ks = smem[slot][0];
-        const uint16_t* Vs = smem[slot][1];
-        const bool is_blk = t >= n_cache_tiles;
-        const int start = is_blk ? 0 : kbeg + t * TK;
-        const int count = is_blk ? p.K : (kend - start < TK ? kend - start : TK);
-
-        // ---- S^T = K Q^T for this wave's key slice ----
-        f32x16 sacc[NBLK];
+    // Tile t's scores: S^T = K Q^T for this wave's key slice of ring slot t.
+    auto qk = [&](int t, f32x16 (&sacc)[NBLK]) {
+        const char* Ks = smem + (t % NSTAGE) * SLOT;
 #pragma unroll
         for (int kb = 0; kb < NBLK; ++kb) {
             const int krow = kg * KPW + kb * 32 + (lane & 31);
@@ -242,7 +308,7 @@ attn_bf16_kernel(AttnParams p)
 #pragma unroll
             for (int ds = 0; ds < D / 16; ++ds) {
                 const int lgr = (2 * ds + half) ^ (krow & (GPR - 1));
-                kf[ds] = *(const u32x4*)(Ks + krow * D + lgr * 8);
+                kf[ds] = *(const u32x4*)(Ks + krow * D * 2 + lgr * 16);
             }
             sacc[kb] = f32x16{};
 #pragma unroll
@@ -250,6 +316,48 @@ attn_bf16_kernel(AttnParams p)
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, kf[ds]), qreg[ds], sacc[kb], 0, 0, 0);
         }
+    };
+    // wait for this lane's loads of tile t (and, for t = 0, the query tile
+    // issued before it), make everyone's visible, and keep the ring full.
+    // Tiles are issued in index order, so last_issued - t tiles may still
+    // fly.  The refill goes to the slot of tile t-2 (NSTAGE = NPRE + 2):
+    // tile t-1 is still being read by this iteration's P V.
+    static_assert(NSTAGE >= NPRE + 2, "software pipelining keeps two tiles resident");
+    auto arrive = [&](int t) {
+        wait_tiles(last_issued - t);
+        __syncthreads();
+        if (t + NPRE < n_tiles) issue(t + NPRE);
+    };
+
+    arrive(0);
+    if constexpr (QLDS) {
+        const char* Qs = smem + NSTAGE * SLOT + rg * 32 * D * 2;
+        const int qrow = lane & 31;
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+            const int gr = (2 * ds + half) ^ ((rg * 32 + qrow) & (GPR - 1));
+            u32x4 v = *(const u32x4*)(Qs + qrow * D * 2 + gr * 16);
+            if (!row_ok) v = u32x4{0, 0, 0, 0};
+            qreg[ds] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    f32x16 scur[NBLK];
+    qk(0, scur);
+
+    for (int t = 0; t < n_tiles; ++t) {
+        // next tile's scores go to the matrix cores while this tile's softmax
+        // runs on the vector ALUs
+        f32x16 snext[NBLK];
+        const bool has_next = t + 1 < n_tiles;
+        if (has_next) {
+            arrive(t + 1);
+            qk(t + 1, snext);
+        }
+
+        const uint16_t* Vs = (const uint16_t*)(smem + (t % NSTAGE) * SLOT + K_BYTES);
+        const bool is_blk = t >= n_cache_tiles;
+        const int start = is_blk ? 0 : kbeg + t * TK;
+        const int count = is_blk ? p.K : (kend - start < TK ? kend - start : TK);
 
         // ---- mask (partial cache tile, or the block tile) ----
         const bool need_mask = is_blk ? (p.mask == 1 || count < TK) : (count < TK);
@@ -261,7 +369,7 @@ attn_bf16_kernel(AttnParams p)
                     const int key = kg * KPW + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
                     bool ok = key < count;
                     if (is_blk && p.mask == 1) ok = ok && key <= qi;
-                    if (!ok) sacc[kb][i] = -INFINITY;
+                    if (!ok) scur[kb][i] = -INFINITY;
                 }
         }
 
@@ -270,7 +378,7 @@ attn_bf16_kernel(AttnParams p)
 #pragma unroll
         for (int kb = 0; kb < NBLK; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, scur[kb][i]);
         {
             auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);
@@ -280,12 +388,11 @@ attn_bf16_kernel(AttnParams p)
             const float m_new = fmaxf(m_run, mx);
             const float corr = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
             m_run = m_new;
-            l_run *= corr;
+            lacc *= corr;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= corr;
         }
         const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-        float psum = 0.f;
         bf16x8 pb[NBLK][2];
 #pragma unroll
         for (int kb = 0; kb < NBLK; ++kb)
@@ -294,22 +401,18 @@ attn_bf16_kernel(AttnParams p)
                 f32x2 pv[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    pv[j][0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * hh + 2 * j], c, -mc));
-                    pv[j][1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * hh + 2 * j + 1], c, -mc));
+                    pv[j][0] = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][8 * hh + 2 * j], c, -mc));
+                    pv[j][1] = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][8 * hh + 2 * j + 1], c, -mc));
                 }
-                uint32_t w[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pv[j], bf16x2));
-                    // the denominator sums the same rounded weights that enter P V,
-                    // so the output stays an exact convex combination of V rows
-                    psum += __uint_as_float(w[j] << 16) + __uint_as_float(w[j] & 0xffff0000u);
-                }
-                pb[kb][hh] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+                const bf16x2 q0 = __builtin_convertvector(pv[0], bf16x2);
+                const bf16x2 q1 = __builtin_convertvector(pv[1], bf16x2);
+                const bf16x2 q2 = __builtin_convertvector(pv[2], bf16x2);
+                const bf16x2 q3 = __builtin_convertvector(pv[3], bf16x2);
+                pb[kb][hh] = bf16x8{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
             }
-        l_run += psum;
 
-        // ---- O^T += V^T P^T ----
+        // ---- O^T += V^T P^T; row sums: (ones) P^T, from the same bf16 weights,
+        // so the output is an exact convex combination of V rows ----
         const int G16 = lane >> 4;
         const int sl = lane & 15;
 #pragma unroll
@@ -326,92 +429,125 @@ attn_bf16_kernel(AttnParams p)
                     for (int ins = 0; ins < 2; ++ins) {
                         const int row = rowbase + 8 * ins;
                         const int gr = (col >> 3) ^ (2 * (row & 3));
-                        const uint16_t* a = Vs + row * D + gr * 8 + (col & 7);
+                        const uint16_t* a = Vs + row * DC + gr * 8 + (col & 7);
                         vv[ins] = __builtin_bit_cast(
                             u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((ORTHRUS_LDS s16x4*)a));
                     }
                     vf[dt] = u32x4{vv[0][0], vv[0][1], vv[1][0], vv[1][1]};
                 }
+                lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[kb][hh], lacc, 0, 0, 0);
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
                     oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8, vf[dt]), pb[kb][hh], oacc[dt], 0, 0, 0);
             }
+        if (has_next) {
+#pragma unroll
+            for (int kb = 0; kb < NBLK; ++kb) scur[kb] = snext[kb];
+        }
     }
+    float l_run = lacc[0];     // every row of ones x P^T holds the query's sum
 
     // ---- merge the key slices of one row group (KS > 1) ----
     if constexpr (KS > 1) {
-        __syncthreads();   // all waves are done with the ring; reuse it
-        float* red = reinterpret_cast<float*>(&smem[0][0][0]);
-        // per row group: [KS-1][NDT*16 + 2][64] floats (accumulators, m, l)
+        // per lane: NDT*16 accumulators, m, l, 2 pad -> 16-byte LDS accesses
         constexpr int ACC = NDT * 16;
-        float* base = red + rg * (KS - 1) * (ACC + 2) * 64;
+        constexpr int LST = ACC + 4;                      // floats per lane record
+        static_assert(NR * (KS - 1) * 64 * LST * 4 <= NSTAGE * SLOT, "merge buffer");
+        __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));
+        __syncthreads();   // all waves are done with the ring; reuse it
+        float* base = reinterpret_cast<float*>(smem) + rg * (KS - 1) * 64 * LST;
         if (kg > 0) {
-            float* mine = base + (kg - 1) * (ACC + 2) * 64;
+            float* mine = base + ((kg - 1) * 64 + lane) * LST;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mine[(dt * 16 + i) * 64 + lane] = oacc[dt][i];
-            mine[ACC * 64 + lane] = m_run;
-            mine[(ACC + 1) * 64 + lane] = l_run;
+                for (int i4 = 0; i4 < 4; ++i4)
+                    *(f32x4*)(mine + dt * 16 + 4 * i4) =
+                        f32x4{oacc[dt][4 * i4], oacc[dt][4 * i4 + 1], oacc[dt][4 * i4 + 2],
+                              oacc[dt][4 * i4 + 3]};
+            *(f32x4*)(mine + ACC) = f32x4{m_run, l_run, 0.f, 0.f};
         }
         __syncthreads();
-        if (kg > 0) return;
+        if (kg == 0) {
 #pragma unroll
-        for (int o = 0; o < KS - 1; ++o) {
-            const float* other = base + o * (ACC + 2) * 64;
-            const float m_o = other[ACC * 64 + lane];
-            const float l_o = other[(ACC + 1) * 64 + lane];
-            const float m_t = fmaxf(m_run, m_o);
-            const float a0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_t) * c);
-            const float a1 = (m_o == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_o - m_t) * c);
+            for (int o = 0; o < KS - 1; ++o) {
+                const float* other = base + (o * 64 + lane) * LST;
+                const f32x4 ml = *(const f32x4*)(other + ACC);
+                const float m_o = ml[0], l_o = ml[1];
+                const float m_t = fmaxf(m_run, m_o);
+                const float a0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_t) * c);
+                const float a1 = (m_o == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_o - m_t) * c);
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
+                for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    oacc[dt][i] = oacc[dt][i] * a0 + other[(dt * 16 + i) * 64 + lane] * a1;
-            l_run = l_run * a0 + l_o * a1;
-            m_run = m_t;
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        const f32x4 v = *(const f32x4*)(other + dt * 16 + 4 * i4);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            oacc[dt][4 * i4 + j] = oacc[dt][4 * i4 + j] * a0 + v[j] * a1;
+                    }
+                l_run = l_run * a0 + l_o * a1;
+                m_run = m_t;
+            }
         }
     }
 
-    // ---- finalize: this lane owns query row r, d = 32dt + 8(i/4) + 4*half + i%4 ----
-    {
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
-                                                   false, false);
-        l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
-    if (!row_ok) return;
+    // ---- finalize: lane owns query row r, columns col0 + 32dt + 8(i/4) + 4*half + i%4 ----
     const float inv = 1.f / l_run;
-    const float lse2 = m_run * c + __builtin_log2f(l_run);
-    if (p.S_grid == 1) {
-        uint16_t* op = (uint16_t*)p.out + (((int64_t)b * p.K + qi) * p.Hq + h) * D + 4 * half;
+    if (p.S_grid > 1) {
+        // split partial, stored in fragment order: each store is 512
+        // contiguous bytes per wave; base-2 lse per row
+        // row groups past Mpad (M not a multiple of the row block) hold no rows
+        if (kg == 0 && rb * QROWS + rg * 32 < p.Mpad) {
+            uint16_t* blk = (uint16_t*)p.ws_o + ((int64_t)bh * p.S_grid + s) * p.Mpad * D;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int i0 = 4 * q4;
+                    const int64_t off = frag_offset(r, col0 + 32 * dt + 8 * q4 + 4 * half, D);
+                    *(u32x2*)(blk + off) =
+                        u32x2{pack_bf16x2(oacc[dt][i0] * inv, oacc[dt][i0 + 1] * inv),
+                              pack_bf16x2(oacc[dt][i0 + 2] * inv, oacc[dt][i0 + 3] * inv)};
+                }
+            if (row_ok && half == 0 && dh == 0)
+                p.ws_lse[((int64_t)bh * p.S_grid + s) * p.Mpad + r] = m_run * c + __builtin_log2f(l_run);
+        }
+        return;
+    }
+    // One split: stage the rows in LDS ([row][DC] with a 16-byte pad) so that
+    // the output stores are whole 16-byte pieces of rows.
+    constexpr int RSTR = DC * 2 + 16;                       // staged row stride, bytes
+    static_assert(QROWS * RSTR <= NSTAGE * SLOT, "staging buffer");
+    __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));
+    __syncthreads();                                        // ring (or merge buffer) free
+    char* stage = smem;
+    if (kg == 0) {
+        char* my = stage + (rg * 32 + (lane & 31)) * RSTR + 8 * half;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int i0 = 4 * q4;
-                const bf16x2 lo = __builtin_convertvector(
-                    (f32x2{oacc[dt][i0] * inv, oacc[dt][i0 + 1] * inv}), bf16x2);
-                const bf16x2 hi = __builtin_convertvector(
-                    (f32x2{oacc[dt][i0 + 2] * inv, oacc[dt][i0 + 3] * inv}), bf16x2);
-                *(u32x2*)(op + 32 * dt + 8 * q4) =
-                    u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+                *(u32x2*)(my + (32 * dt + 8 * q4) * 2) =
+                    u32x2{pack_bf16x2(oacc[dt][i0] * inv, oacc[dt][i0 + 1] * inv),
+                          pack_bf16x2(oacc[dt][i0 + 2] * inv, oacc[dt][i0 + 3] * inv)};
             }
-        if (p.lse && half == 0) p.lse[((int64_t)b * p.Hq + h) * p.K + qi] = lse2 * kLn2;
-    } else {
-        const int64_t prow = ((int64_t)bh * p.M + r) * p.S_grid + s;
-        float* op = p.ws_o + prow * D + 4 * half;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int i0 = 4 * q4;
-                f32x4 v = {oacc[dt][i0] * inv, oacc[dt][i0 + 1] * inv, oacc[dt][i0 + 2] * inv,
-                           oacc[dt][i0 + 3] * inv};
-                *(f32x4*)(op + 32 * dt + 8 * q4) = v;
-            }
-        if (half == 0) p.ws_lse[prow] = lse2;
+        if (row_ok && half == 0 && dh == 0 && p.lse)
+            p.lse[((int64_t)b * p.Hq + h) * p.K + qi] = (m_run * c + __builtin_log2f(l_run)) * kLn2;
+    }
+    __syncthreads();
+    constexpr int PIECES = DC * 2 / 16;                     // 16-byte pieces per row
+    for (int idx = tid; idx < QROWS * PIECES; idx += 64 * NW) {
+        const int row = idx / PIECES;
+        const int pc = idx % PIECES;
+        const int rr = rb * QROWS + row;
+        if (rr >= p.M) continue;
+        const u32x4 v = *(const u32x4*)(stage + row * RSTR + pc * 16);
+        const int hh_ = g * p.G + rr / p.K;
+        uint16_t* dst = (uint16_t*)p.out + (((int64_t)b * p.K + rr % p.K) * p.Hq + hh_) * D;
+        *(u32x4*)(dst + col0 + pc * 8) = v;
     }
 }
 
@@ -551,10 +687,10 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams p)
             for (int k = 0; k < DC; ++k) op[lane + 64 * k] = o[j][k] * inv;
             if (p.lse && lane == 0) p.lse[((int64_t)b * p.Hq + h) * p.K + qi] = lse2 * kLn2;
         } else {
-            const int64_t prow = ((int64_t)bh * p.M + rr) * p.S_grid + s;
+            float* blk = (float*)p.ws_o + ((int64_t)bh * p.S_grid + s) * p.Mpad * D;
 #pragma unroll
-            for (int k = 0; k < DC; ++k) p.ws_o[prow * D + lane + 64 * k] = o[j][k] * inv;
-            if (lane == 0) p.ws_lse[prow] = lse2;
+            for (int k = 0; k < DC; ++k) blk[frag_offset(rr, lane + 64 * k, D)] = o[j][k] * inv;
+            if (lane == 0) p.ws_lse[((int64_t)bh * p.S_grid + s) * p.Mpad + rr] = lse2;
         }
     }
 }
@@ -562,49 +698,65 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams p)
 // --------------------------------------------------------------------------
 // split-KV merge: lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s
 // --------------------------------------------------------------------------
-// Partials are [B*Hkv][M][S_grid][D] (one row's splits contiguous) with base-2
-// lse [B*Hkv][M][S_grid].  A work-group of 128 threads merges 128/(D/4) rows;
-// each thread owns 4 columns of one row and keeps 8 split loads in flight.
+// Partial blocks [B*Hkv][S_grid][Mpad x D] in fragment order (bf16 on the bf16
+// path, fp32 on the fp32 path), base-2 lse [B*Hkv][S_grid][Mpad].  A work-group
+// of 128 threads covers 32 rows x 16 columns: thread = (row q, 4 columns), so
+// 32 consecutive threads read one contiguous run of a partial block (and of
+// the lse); each thread issues the loads of up to UNROLL splits at once.
 template <int D, bool BF16>
 __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
 {
-    constexpr int TPR = D / 4;          // threads per row (4 floats each)
-    constexpr int RPB = 128 / TPR;      // rows per block
-    constexpr int UNROLL = 8;
+    constexpr int UNROLL = BF16 ? 32 : 16;
     const int bh = blockIdx.x;
     const int b = bh / p.Hkv;
     const int g = bh % p.Hkv;
-    const int r = blockIdx.y * RPB + threadIdx.x / TPR;
-    const int d = (threadIdx.x % TPR) * 4;
+    const int rgrp = blockIdx.y / (D / 16);
+    const int cgrp = blockIdx.y % (D / 16);
+    const int q = threadIdx.x & 31;
+    const int quad = threadIdx.x >> 5;                 // 0..3: 4 columns each
+    const int r = rgrp * 32 + q;
+    const int d = cgrp * 16 + quad * 4;
     if (r >= p.M) return;
     const int L = p.lens[b];
     int S_b = (L + p.SL - 1) / p.SL;
     S_b = S_b < 1 ? 1 : (S_b > p.S_grid ? p.S_grid : S_b);
-    const int64_t row = (int64_t)bh * p.M + r;
-    const float* lse_r = p.ws_lse + row * p.S_grid;
-    const float* o_r = p.ws_o + row * p.S_grid * D + d;
+    const float* lse_r = p.ws_lse + (int64_t)bh * p.S_grid * p.Mpad + r;   // split sp at + sp*Mpad
+    const int64_t blk0 = (int64_t)bh * p.S_grid * p.Mpad * D + frag_offset(r, d, D);
+    const int64_t bstride = (int64_t)p.Mpad * D;
+    auto part = [&](int sp) -> f32x4 {
+        if (BF16) {
+            const u32x2 v = *(const u32x2*)((const uint16_t*)p.ws_o + blk0 + sp * bstride);
+            return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                         __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+        }
+        return *(const f32x4*)((const float*)p.ws_o + blk0 + sp * bstride);
+    };
     float mx = -INFINITY;
-    for (int s = 0; s < S_b; ++s) mx = fmaxf(mx, lse_r[s]);
     float W = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    for (; s + UNROLL <= S_b; s += UNROLL) {
+    for (int s0 = 0; s0 < S_b; s0 += UNROLL) {
         f32x4 v[UNROLL];
-        float w[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) v[u] = *(const f32x4*)(o_r + (int64_t)(s + u) * D);
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) w[u] = __builtin_amdgcn_exp2f(lse_r[s + u] - mx);
+        float l2[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            W += w[u];
-            acc += w[u] * v[u];
+            const int sp = s0 + u < S_b ? s0 + u : S_b - 1;
+            l2[u] = s0 + u < S_b ? lse_r[(int64_t)sp * p.Mpad] : -INFINITY;
+            v[u] = part(sp);
         }
-    }
-    for (; s < S_b; ++s) {
-        const float w = __builtin_amdgcn_exp2f(lse_r[s] - mx);
-        W += w;
-        acc += w * *(const f32x4*)(o_r + (int64_t)s * D);
+        float gm = l2[0];
+#pragma unroll
+        for (int u = 1; u < UNROLL; ++u) gm = fmaxf(gm, l2[u]);
+        const float m_new = fmaxf(mx, gm);
+        const float corr = (mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mx - m_new);
+        W *= corr;
+        acc *= corr;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const float w = __builtin_amdgcn_exp2f(l2[u] - m_new);   // 0 for padding
+            W += w;
+            acc += w * v[u];
+        }
+        mx = m_new;
     }
     const float inv = 1.f / W;
     const int hl = r / p.K, qi = r % p.K;
@@ -622,24 +774,46 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
 // --------------------------------------------------------------------------
 // launch
 // --------------------------------------------------------------------------
-template <int D, int NR, int KS>
+// Deepest K/V ring that fits the 160 KiB of LDS next to the query tile and the
+// page-id staging (and the DMA counter range).
+constexpr int ring_depth(int D, int NR, int KS, int DS, bool paged, bool qlds) {
+    const int slot = 64 * D * 2 + 64 * (D / DS) * 2;
+    const int q = qlds ? 32 * NR * D * 2 : 0;
+    const int pages = paged ? kMaxSplitPages * 4 : 0;
+    int n = (163840 - q - pages) / slot;
+    n = n > 6 ? 6 : n;
+    const int lpt = (D / 8 + D / DS / 8) / (NR * KS);
+    const int lq = qlds ? 32 * NR * D * 2 / 1024 / (NR * KS) : 0;
+    while (n > 3 && lpt * 3 + lq > 63) --n;
+    return n;
+}
+
+template <int D, int NR, int KS, int DS, bool QLDS>
 static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
-    dim3 grid(p.S_grid * p.B * p.Hkv, p.row_blocks);
-    constexpr int NSTAGE = 4;
-    if (p.layout == 1)
-        hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, NSTAGE, true>), grid, dim3(64 * NR * KS), 0, st, p);
-    else
-        hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, NSTAGE, false>), grid, dim3(64 * NR * KS), 0, st, p);
+    dim3 grid(p.S_grid * p.B * p.Hkv, p.row_blocks * DS);
+    dim3 block(64 * NR * KS);
+    if (p.layout == 1) {
+        constexpr int NS = ring_depth(D, NR, KS, DS, true, QLDS);
+        constexpr int NP = NS - 2 < 2 ? NS - 2 : 2;
+        hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, DS, NS, NP, true, QLDS>), grid, block, 0, st, p);
+    } else {
+        constexpr int NS = ring_depth(D, NR, KS, DS, false, QLDS);
+        constexpr int NP = NS - 2 < 2 ? NS - 2 : 2;
+        hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, DS, NS, NP, false, QLDS>), grid, block, 0, st, p);
+    }
     return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_bf16_d(const AttnParams& p, hipStream_t st) {
     switch (p.rows_per_wg) {
-        case 32: return launch_bf16<D, 1, 2>(p, st);
-        case 64: return launch_bf16<D, 2, 2>(p, st);
-        case 128: return launch_bf16<D, 4, 2>(p, st);
-        default: return launch_bf16<D, 8, 1>(p, st);
+        case 32: return launch_bf16<D, 1, 2, 1, true>(p, st);
+        case 64: return launch_bf16<D, 2, 2, 1, true>(p, st);
+        case 128:
+            if constexpr (D == 128)
+                if (p.ds == 2) return launch_bf16<D, 4, 2, 2, true>(p, st);
+            return launch_bf16<D, 4, 2, 1, true>(p, st);
+        default: return launch_bf16<D, 8, 1, 1, false>(p, st);
     }
 }
 
@@ -662,8 +836,7 @@ hipError_t launch_block_attn(const AttnParams& p, int dtype, hipStream_t st) {
         e = hipGetLastError();
     }
     if (e != hipSuccess || p.S_grid == 1) return e;
-    const int rpb = 128 / (p.D / 4);
-    dim3 mgrid(p.B * p.Hkv, (p.M + rpb - 1) / rpb);
+    dim3 mgrid(p.B * p.Hkv, (p.Mpad / 32) * (p.D / 16));
     if (p.D == 128) {
         if (dtype == 1) hipLaunchKernelGGL((attn_merge_kernel<128, true>), mgrid, dim3(128), 0, st, p);
         else hipLaunchKernelGGL((attn_merge_kernel<128, false>), mgrid, dim3(128), 0, st, p);

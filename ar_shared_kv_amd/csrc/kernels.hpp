@@ -22,13 +22,14 @@ struct AttnParams {
     const int32_t *lens;              // [B]
     void *out;                        // [B][K][Hq][D]
     float *lse;                       // [B][Hq][K] or null
-    float *ws_o;                      // split partials [B*Hkv][M][S_grid][D]
-    float *ws_lse;                    // [B*Hkv][M][S_grid] (base-2 units)
-    int B, K, Hq, Hkv, G, M, D;
+    void *ws_o;                       // split partials [B*Hkv][S_grid][Mpad x D] fragment order
+    float *ws_lse;                    // [B*Hkv][S_grid][Mpad] (base-2 units)
+    int B, K, Hq, Hkv, G, M, Mpad, D;   // Mpad = M rounded up to 32
     int64_t cap, maxp;
     int layout, mask;
     int SL, S_grid;                   // keys per split (multiple of 64), grid splits
     int rows_per_wg, row_blocks;
+    int ds;                           // output-column split (1 or 2)
     float c;                          // scale * log2(e)
 };
 

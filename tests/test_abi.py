@@ -76,9 +76,13 @@ def test_block_attn_validation_codes():
 
 def test_block_attn_workspace_formula():
     c = cache(capacity=131136, max_len=131072)
-    # 64 splits of 2048 keys: partials [B*Hkv][S][M][D] + lse [B*Hkv][S][M], fp32
+    # 64 splits of 2048 keys: bf16 partials [B*Hkv][M][S][D] (256-byte aligned
+    # end) + fp32 lse [B*Hkv][M][S]
     n = B.orthrus_block_attn_workspace_bytes(c, 1, 64, 32, 8, 128, B.BF16, 64)
-    assert n == 1 * 8 * 64 * 256 * 129 * 4
+    rows = 1 * 8 * 64 * 256
+    assert n == -(-rows * 128 * 2 // 256) * 256 + rows * 4
+    nf = B.orthrus_block_attn_workspace_bytes(c, 1, 64, 32, 8, 128, B.F32, 64)
+    assert nf == -(-rows * 128 * 4 // 256) * 256 + rows * 4
     # one split -> no workspace
     small = cache(capacity=128, max_len=128)
     assert B.orthrus_block_attn_workspace_bytes(small, 1, 8, 2, 1, 64, B.F32, 0) == 0

@@ -107,6 +107,8 @@ EDGE = [
     ("K64-G16-M1024", 1, 16, 1, 64, 64, [300], "bf16", False),
     ("D64", 2, 8, 2, 64, 16, [333, 90], "bf16", False),
     ("G1", 1, 4, 4, 128, 32, [500], "bf16", False),
+    ("M96-rowblock-tail", 1, 24, 8, 128, 32, [900], "bf16", False),
+    ("M48", 2, 12, 4, 128, 16, [1500, 40], "bf16", False),
     ("paged-ragged", 4, 8, 2, 128, 9, [0, 17, 300, 1100], "bf16", True),
     ("paged-D64", 2, 4, 1, 64, 32, [16, 47], "bf16", True),
     ("fp32-ragged", 2, 4, 2, 128, 5, [70, 3], "f32", False),

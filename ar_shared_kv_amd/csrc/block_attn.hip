@@ -85,6 +85,11 @@ attn_bf16_kernel(AttnParams p)
     constexpr int QROWS = 32 * NR;
     constexpr int Q_BYTES = QLDS ? QROWS * D * 2 : 0;
     constexpr int CQ = Q_BYTES / 1024;         // query chunks
+    // paged: the query tile borrows ring slot NSTAGE-1 (the page ids take the
+    // room a separate query buffer would need); contiguous: its own buffer
+    constexpr bool QSLOT = QLDS && PAGED;
+    constexpr int Q_EXTRA = QSLOT ? 0 : Q_BYTES;
+    static_assert(!QSLOT || Q_BYTES <= SLOT, "the query tile fits one ring slot");
     static_assert(KPW % 32 == 0, "each wave needs whole 32-key blocks");
     static_assert(CK % NW == 0 && CV % NW == 0 && CQ % NW == 0, "chunks must split evenly");
     static_assert(NPRE >= 1 && NPRE < NSTAGE, "prefetch depth");
@@ -96,8 +101,9 @@ attn_bf16_kernel(AttnParams p)
     constexpr float kLazy = 8.0f;
 
     constexpr int PAGE_BYTES = PAGED ? kMaxSplitPages * 4 : 0;
-    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * SLOT + Q_BYTES + PAGE_BYTES];
-    int* s_pages = reinterpret_cast<int*>(smem + NSTAGE * SLOT + Q_BYTES);   // PAGED only
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * SLOT + Q_EXTRA + PAGE_BYTES];
+    int* s_pages = reinterpret_cast<int*>(smem + NSTAGE * SLOT + Q_EXTRA);   // PAGED only
+    constexpr int Q_OFF = QSLOT ? (NSTAGE - 1) * SLOT : NSTAGE * SLOT;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -122,7 +128,7 @@ attn_bf16_kernel(AttnParams p)
     const int qi = row_ok ? r % p.K : 0;
     const int h = g * p.G + hl;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(ORTHRUS_LDS void*)&smem[0];
-    const uint32_t q_lds = lds_base + NSTAGE * SLOT;
+    const uint32_t q_lds = lds_base + Q_OFF;
     bf16x8 qreg[D / 16];
     if constexpr (QLDS) {
         // DMA the query tile (rows XOR-swizzled like K) ahead of the K/V ring
@@ -246,6 +252,7 @@ attn_bf16_kernel(AttnParams p)
         }
     };
     static_assert(NPRE <= 4, "wait_tiles covers up to 4 pending tiles");
+    static_assert(!QSLOT || NPRE <= NSTAGE - 2, "the query slot must not be in the prologue");
 
     // ---- prologue: NPRE tiles in flight; iteration t issues tile t + NPRE
     // into the slot of an already consumed tile (NPRE < NSTAGE) ----
@@ -331,7 +338,9 @@ attn_bf16_kernel(AttnParams p)
 
     arrive(0);
     if constexpr (QLDS) {
-        const char* Qs = smem + NSTAGE * SLOT + rg * 32 * D * 2;
+        // in ring slot NSTAGE-1 it is first overwritten by tile NSTAGE-1, issued
+        // after a barrier that every wave passes once it has read its query rows
+        const char* Qs = smem + Q_OFF + rg * 32 * D * 2;
         const int qrow = lane & 31;
 #pragma unroll
         for (int ds = 0; ds < D / 16; ++ds) {
@@ -448,49 +457,53 @@ attn_bf16_kernel(AttnParams p)
     }
     float l_run = lacc[0];     // every row of ones x P^T holds the query's sum
 
-    // ---- merge the key slices of one row group (KS > 1) ----
+    // ---- merge the two key slices of one row group (KS = 2) ----
+    // Each slice finalizes half of the D tiles: it hands the other half of
+    // its accumulators (and its m, l) to the other slice through LDS and
+    // takes the other slice's accumulators for its own half.
+    constexpr int HALF_DT = KS > 1 ? NDT / 2 : NDT;
+    // does this wave write D tile dt of the result?
+    auto owns = [&](int dt) { return KS == 1 || ((dt < HALF_DT) == (kg == 0)); };
     if constexpr (KS > 1) {
-        // per lane: NDT*16 accumulators, m, l, 2 pad -> 16-byte LDS accesses
-        constexpr int ACC = NDT * 16;
-        constexpr int LST = ACC + 4;                      // floats per lane record
-        static_assert(NR * (KS - 1) * 64 * LST * 4 <= NSTAGE * SLOT, "merge buffer");
+        static_assert(KS == 2 && NDT % 2 == 0, "two key slices, even number of D tiles");
+        constexpr int REC = HALF_DT * 16 + 4;             // floats per lane record
+        static_assert(NR * 2 * 64 * REC * 4 <= NSTAGE * SLOT, "merge buffer");
         __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));
         __syncthreads();   // all waves are done with the ring; reuse it
-        float* base = reinterpret_cast<float*>(smem) + rg * (KS - 1) * 64 * LST;
-        if (kg > 0) {
-            float* mine = base + ((kg - 1) * 64 + lane) * LST;
+        float* base = reinterpret_cast<float*>(smem) + rg * 2 * 64 * REC;
+        float* mine = base + (kg * 64 + lane) * REC;
+        const float* other = base + ((1 - kg) * 64 + lane) * REC;
+        auto put = [&](int dt0) {
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
+            for (int j = 0; j < HALF_DT; ++j)
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4)
-                    *(f32x4*)(mine + dt * 16 + 4 * i4) =
-                        f32x4{oacc[dt][4 * i4], oacc[dt][4 * i4 + 1], oacc[dt][4 * i4 + 2],
-                              oacc[dt][4 * i4 + 3]};
-            *(f32x4*)(mine + ACC) = f32x4{m_run, l_run, 0.f, 0.f};
-        }
+                    *(f32x4*)(mine + j * 16 + 4 * i4) =
+                        f32x4{oacc[dt0 + j][4 * i4], oacc[dt0 + j][4 * i4 + 1],
+                              oacc[dt0 + j][4 * i4 + 2], oacc[dt0 + j][4 * i4 + 3]};
+        };
+        if (kg == 0) put(HALF_DT); else put(0);
+        *(f32x4*)(mine + HALF_DT * 16) = f32x4{m_run, l_run, 0.f, 0.f};
         __syncthreads();
-        if (kg == 0) {
+        const f32x4 ml = *(const f32x4*)(other + HALF_DT * 16);
+        const float m_o = ml[0], l_o = ml[1];
+        const float m_t = fmaxf(m_run, m_o);
+        const float a0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_t) * c);
+        const float a1 = (m_o == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_o - m_t) * c);
+        auto take = [&](int dt0) {
 #pragma unroll
-            for (int o = 0; o < KS - 1; ++o) {
-                const float* other = base + (o * 64 + lane) * LST;
-                const f32x4 ml = *(const f32x4*)(other + ACC);
-                const float m_o = ml[0], l_o = ml[1];
-                const float m_t = fmaxf(m_run, m_o);
-                const float a0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_t) * c);
-                const float a1 = (m_o == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_o - m_t) * c);
+            for (int j = 0; j < HALF_DT; ++j)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x4 v = *(const f32x4*)(other + j * 16 + 4 * i4);
 #pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4) {
-                        const f32x4 v = *(const f32x4*)(other + dt * 16 + 4 * i4);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            oacc[dt][4 * i4 + j] = oacc[dt][4 * i4 + j] * a0 + v[j] * a1;
-                    }
-                l_run = l_run * a0 + l_o * a1;
-                m_run = m_t;
-            }
-        }
+                    for (int e = 0; e < 4; ++e)
+                        oacc[dt0 + j][4 * i4 + e] = oacc[dt0 + j][4 * i4 + e] * a0 + v[e] * a1;
+                }
+        };
+        if (kg == 0) take(0); else take(HALF_DT);
+        l_run = l_run * a0 + l_o * a1;
+        m_run = m_t;
     }
 
     // ---- finalize: lane owns query row r, columns col0 + 32dt + 8(i/4) + 4*half + i%4 ----
@@ -499,10 +512,11 @@ attn_bf16_kernel(AttnParams p)
         // split partial, stored in fragment order: each store is 512
         // contiguous bytes per wave; base-2 lse per row
         // row groups past Mpad (M not a multiple of the row block) hold no rows
-        if (kg == 0 && rb * QROWS + rg * 32 < p.Mpad) {
+        if (rb * QROWS + rg * 32 < p.Mpad) {
             uint16_t* blk = (uint16_t*)p.ws_o + ((int64_t)bh * p.S_grid + s) * p.Mpad * D;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
+                if (owns(dt))
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int i0 = 4 * q4;
@@ -511,7 +525,7 @@ attn_bf16_kernel(AttnParams p)
                         u32x2{pack_bf16x2(oacc[dt][i0] * inv, oacc[dt][i0 + 1] * inv),
                               pack_bf16x2(oacc[dt][i0 + 2] * inv, oacc[dt][i0 + 3] * inv)};
                 }
-            if (row_ok && half == 0 && dh == 0)
+            if (row_ok && half == 0 && dh == 0 && kg == 0)
                 p.ws_lse[((int64_t)bh * p.S_grid + s) * p.Mpad + r] = m_run * c + __builtin_log2f(l_run);
         }
         return;
@@ -523,10 +537,11 @@ attn_bf16_kernel(AttnParams p)
     __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));
     __syncthreads();                                        // ring (or merge buffer) free
     char* stage = smem;
-    if (kg == 0) {
+    {
         char* my = stage + (rg * 32 + (lane & 31)) * RSTR + 8 * half;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
+            if (owns(dt))
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int i0 = 4 * q4;
@@ -534,7 +549,7 @@ attn_bf16_kernel(AttnParams p)
                     u32x2{pack_bf16x2(oacc[dt][i0] * inv, oacc[dt][i0 + 1] * inv),
                           pack_bf16x2(oacc[dt][i0 + 2] * inv, oacc[dt][i0 + 3] * inv)};
             }
-        if (row_ok && half == 0 && dh == 0 && p.lse)
+        if (row_ok && half == 0 && dh == 0 && kg == 0 && p.lse)
             p.lse[((int64_t)b * p.Hq + h) * p.K + qi] = (m_run * c + __builtin_log2f(l_run)) * kLn2;
     }
     __syncthreads();
@@ -774,18 +789,23 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
 // --------------------------------------------------------------------------
 // launch
 // --------------------------------------------------------------------------
-// Deepest K/V ring that fits the 160 KiB of LDS next to the query tile and the
-// page-id staging (and the DMA counter range).
-constexpr int ring_depth(int D, int NR, int KS, int DS, bool paged, bool qlds) {
+// Deepest K/V ring that fits the 160 KiB of LDS next to the page-id staging
+// (paged) or the query tile (contiguous).
+constexpr int ring_depth(int D, int NR, int DS, bool paged, bool qlds) {
     const int slot = 64 * D * 2 + 64 * (D / DS) * 2;
-    const int q = qlds ? 32 * NR * D * 2 : 0;
-    const int pages = paged ? kMaxSplitPages * 4 : 0;
-    int n = (163840 - q - pages) / slot;
-    n = n > 6 ? 6 : n;
+    const int extra = paged ? kMaxSplitPages * 4 : (qlds ? 32 * NR * D * 2 : 0);
+    const int n = (163840 - extra) / slot;
+    return n > 6 ? 6 : n;
+}
+// Tiles in flight ahead of the one computed: at most 2 (deeper prefetch only
+// adds to the queueing in HBM when every CU streams) and NSTAGE - 2 (the
+// software pipeline keeps two tiles resident), within the DMA counter range.
+constexpr int prefetch_depth(int D, int NR, int KS, int DS, int nstage, bool qlds) {
     const int lpt = (D / 8 + D / DS / 8) / (NR * KS);
     const int lq = qlds ? 32 * NR * D * 2 / 1024 / (NR * KS) : 0;
-    while (n > 3 && lpt * 3 + lq > 63) --n;
-    return n;
+    int np = nstage - 2 < 2 ? nstage - 2 : 2;
+    while (np > 1 && lpt * (np + 1) + lq > 63) --np;
+    return np;
 }
 
 template <int D, int NR, int KS, int DS, bool QLDS>
@@ -793,12 +813,12 @@ static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
     dim3 grid(p.S_grid * p.B * p.Hkv, p.row_blocks * DS);
     dim3 block(64 * NR * KS);
     if (p.layout == 1) {
-        constexpr int NS = ring_depth(D, NR, KS, DS, true, QLDS);
-        constexpr int NP = NS - 2 < 2 ? NS - 2 : 2;
+        constexpr int NS = ring_depth(D, NR, DS, true, QLDS);
+        constexpr int NP = prefetch_depth(D, NR, KS, DS, NS, QLDS);
         hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, DS, NS, NP, true, QLDS>), grid, block, 0, st, p);
     } else {
-        constexpr int NS = ring_depth(D, NR, KS, DS, false, QLDS);
-        constexpr int NP = NS - 2 < 2 ? NS - 2 : 2;
+        constexpr int NS = ring_depth(D, NR, DS, false, QLDS);
+        constexpr int NP = prefetch_depth(D, NR, KS, DS, NS, QLDS);
         hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, DS, NS, NP, false, QLDS>), grid, block, 0, st, p);
     }
     return hipGetLastError();
@@ -809,10 +829,7 @@ static hipError_t launch_bf16_d(const AttnParams& p, hipStream_t st) {
     switch (p.rows_per_wg) {
         case 32: return launch_bf16<D, 1, 2, 1, true>(p, st);
         case 64: return launch_bf16<D, 2, 2, 1, true>(p, st);
-        case 128:
-            if constexpr (D == 128)
-                if (p.ds == 2) return launch_bf16<D, 4, 2, 2, true>(p, st);
-            return launch_bf16<D, 4, 2, 1, true>(p, st);
+        case 128: return launch_bf16<D, 4, 2, 1, true>(p, st);
         default: return launch_bf16<D, 8, 1, 1, false>(p, st);
     }
 }

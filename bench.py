@@ -26,6 +26,35 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verify steps/s and achieved HBM TB/s, block attn+consensus, K=32, Qwen3-8B shape"
 HBM_PEAK_GBPS = 8000.0
+# sources that decide what the block-attention launch does (kernel and plan)
+ATTN_SOURCES = ("ar_shared_kv_amd/csrc/block_attn.hip", "ar_shared_kv_amd/csrc/kernels.hpp",
+                "ar_shared_kv_amd/csrc/common.hpp", "ar_shared_kv_amd/csrc/abi.cpp")
+
+
+def attn_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, splits):
+    """HBM bytes per block-attention launch from the committed counter summary
+    of this workload, or None when the kernel sources changed since then."""
+    path = os.path.join(ROOT, "profiles", f"block_attn_{workload}_traffic.txt")
+    if splits or not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_hash") != attn_source_hash():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def parse():
@@ -39,6 +68,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-bytes", type=int, default=0,
+                    help="first run one plain device copy of this many bytes (a known-size "
+                         "kernel for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -229,6 +261,14 @@ def main():
         cfg = cfg.with_(K=args.K)
     splits = args.splits or cfg.num_splits
     log(f"workload {cfg.name} K={cfg.K} splits={splits or 'auto'}")
+    if args.calib_bytes:
+        # an elementwise kernel that reads and writes calib_bytes once each
+        src = torch.ones(args.calib_bytes // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     step = Step(cfg, splits)
     graph = not args.no_graph
 
@@ -262,7 +302,7 @@ def main():
                    "num_splits": splits or "auto", "graph": graph},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(cfg.name, args.splits),
                      "kernel": "block attention (attn_bf16_kernel + split merge), per launch",
                      "us_per_launch": round(us_attn, 3), "bytes_per_launch": attn_b,
                      "mfma_frac": round(attn_f / (us_attn * 1e-6) / 2.5e15, 4)},

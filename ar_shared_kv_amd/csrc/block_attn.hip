@@ -327,9 +327,10 @@ attn_bf16_kernel(AttnParams p)
     // wait for this lane's loads of tile t (and, for t = 0, the query tile
     // issued before it), make everyone's visible, and keep the ring full.
     // Tiles are issued in index order, so last_issued - t tiles may still
-    // fly.  The refill goes to the slot of tile t-2 (NSTAGE = NPRE + 2):
-    // tile t-1 is still being read by this iteration's P V.
-    static_assert(NSTAGE >= NPRE + 2, "software pipelining keeps two tiles resident");
+    // fly.  arrive(t) comes after every wave has issued its P V of tile t-1,
+    // whose operands are then in registers, so the refill (tile t + NPRE)
+    // may take the slot of tile t-1 (NSTAGE = NPRE + 1).
+    static_assert(NSTAGE >= NPRE + 1, "ring slots for the tiles in flight");
     auto arrive = [&](int t) {
         wait_tiles(last_issued - t);
         __syncthreads();
@@ -354,14 +355,6 @@ attn_bf16_kernel(AttnParams p)
     qk(0, scur);
 
     for (int t = 0; t < n_tiles; ++t) {
-        // next tile's scores go to the matrix cores while this tile's softmax
-        // runs on the vector ALUs
-        f32x16 snext[NBLK];
-        const bool has_next = t + 1 < n_tiles;
-        if (has_next) {
-            arrive(t + 1);
-            qk(t + 1, snext);
-        }
 
         const uint16_t* Vs = (const uint16_t*)(smem + (t % NSTAGE) * SLOT + K_BYTES);
         const bool is_blk = t >= n_cache_tiles;
@@ -450,9 +443,12 @@ attn_bf16_kernel(AttnParams p)
                     oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8, vf[dt]), pb[kb][hh], oacc[dt], 0, 0, 0);
             }
-        if (has_next) {
-#pragma unroll
-            for (int kb = 0; kb < NBLK; ++kb) scur[kb] = snext[kb];
+        // Only now wait for the next tile: everything this tile allows is
+        // issued, so after the last tile lands only its own work remains.  Its
+        // scores go to the matrix cores behind this tile's P V.
+        if (t + 1 < n_tiles) {
+            arrive(t + 1);
+            qk(t + 1, scur);
         }
     }
     float l_run = lacc[0];     // every row of ones x P^T holds the query's sum
@@ -797,13 +793,15 @@ constexpr int ring_depth(int D, int NR, int DS, bool paged, bool qlds) {
     const int n = (163840 - extra) / slot;
     return n > 6 ? 6 : n;
 }
-// Tiles in flight ahead of the one computed: at most 2 (deeper prefetch only
-// adds to the queueing in HBM when every CU streams) and NSTAGE - 2 (the
-// software pipeline keeps two tiles resident), within the DMA counter range.
-constexpr int prefetch_depth(int D, int NR, int KS, int DS, int nstage, bool qlds) {
+// Tiles in flight ahead of the one computed: 2 (with every CU streaming, a
+// deeper queue delays the first tiles more than it speeds up the last),
+// NSTAGE - 2 when the query tile sits in the last slot (it is read after the
+// first refill could be issued otherwise), within the DMA counter range.
+constexpr int prefetch_depth(int D, int NR, int KS, int DS, int nstage, bool qslot) {
     const int lpt = (D / 8 + D / DS / 8) / (NR * KS);
-    const int lq = qlds ? 32 * NR * D * 2 / 1024 / (NR * KS) : 0;
-    int np = nstage - 2 < 2 ? nstage - 2 : 2;
+    const int lq = 32 * NR * D * 2 / 1024 / (NR * KS);
+    int np = qslot ? nstage - 2 : nstage - 1;
+    np = np > 2 ? 2 : np;
     while (np > 1 && lpt * (np + 1) + lq > 63) --np;
     return np;
 }
@@ -818,7 +816,7 @@ static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
         hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, DS, NS, NP, true, QLDS>), grid, block, 0, st, p);
     } else {
         constexpr int NS = ring_depth(D, NR, DS, false, QLDS);
-        constexpr int NP = prefetch_depth(D, NR, KS, DS, NS, QLDS);
+        constexpr int NP = prefetch_depth(D, NR, KS, DS, NS, false);
         hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, DS, NS, NP, false, QLDS>), grid, block, 0, st, p);
     }
     return hipGetLastError();

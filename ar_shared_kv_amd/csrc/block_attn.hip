@@ -728,9 +728,6 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
     const int r = rgrp * 32 + q;
     const int d = cgrp * 16 + quad * 4;
     if (r >= p.M) return;
-    const int L = p.lens[b];
-    int S_b = (L + p.SL - 1) / p.SL;
-    S_b = S_b < 1 ? 1 : (S_b > p.S_grid ? p.S_grid : S_b);
     const float* lse_r = p.ws_lse + (int64_t)bh * p.S_grid * p.Mpad + r;   // split sp at + sp*Mpad
     const int64_t blk0 = (int64_t)bh * p.S_grid * p.Mpad * D + frag_offset(r, d, D);
     const int64_t bstride = (int64_t)p.Mpad * D;
@@ -742,18 +739,34 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
         }
         return *(const f32x4*)((const float*)p.ws_o + blk0 + sp * bstride);
     };
+    f32x4 v[UNROLL];
+    float l2[UNROLL];
+    auto load = [&](int s0) {   // splits s0.. (clamped into the grid)
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int sp = s0 + u < p.S_grid ? s0 + u : p.S_grid - 1;
+            l2[u] = lse_r[(int64_t)sp * p.Mpad];
+            v[u] = part(sp);
+        }
+    };
+    // The first chunk does not depend on lens[b] (splits past S_b are read,
+    // then discarded): issue it first so that its round trip and the one of
+    // lens overlap.
+    load(0);
+    asm volatile("" ::: "memory");
+    const int L = ((const __attribute__((address_space(4))) int32_t*)p.lens)[b];
+    int S_b = (L + p.SL - 1) / p.SL;
+    S_b = S_b < 1 ? 1 : (S_b > p.S_grid ? p.S_grid : S_b);
     float mx = -INFINITY;
     float W = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < S_b; s0 += UNROLL) {
-        f32x4 v[UNROLL];
-        float l2[UNROLL];
+    for (int s0 = 0;;) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int sp = s0 + u < S_b ? s0 + u : S_b - 1;
-            l2[u] = s0 + u < S_b ? lse_r[(int64_t)sp * p.Mpad] : -INFINITY;
-            v[u] = part(sp);
-        }
+        for (int u = 0; u < UNROLL; ++u)
+            if (s0 + u >= S_b) {     // past this request's splits (stale workspace)
+                l2[u] = -INFINITY;
+                v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         float gm = l2[0];
 #pragma unroll
         for (int u = 1; u < UNROLL; ++u) gm = fmaxf(gm, l2[u]);
@@ -768,6 +781,9 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
             acc += w * v[u];
         }
         mx = m_new;
+        s0 += UNROLL;
+        if (s0 >= S_b) break;
+        load(s0);
     }
     const float inv = 1.f / W;
     const int hl = r / p.K, qi = r % p.K;

@@ -12,16 +12,17 @@
 //    contraction is dense: bf16 MFMA 32x32x16 for S^T = K Q^T and
 //    O^T += V^T P^T with fp32 accumulation.
 //  * K/V tiles of 64 keys stream HBM -> LDS with global_load_lds (16 B per
-//    lane, no VGPR staging) through an NSTAGE-deep ring, so several tiles are
-//    in flight per CU.  K is XOR-swizzled per row for conflict-free 16-byte
+//    lane, no VGPR staging) through an NSTAGE-deep ring, NPRE tiles ahead of
+//    the one computed.  K is XOR-swizzled per row for conflict-free 16-byte
 //    reads; V is read transposed with ds_read_b64_tr_b16 straight into the
 //    MFMA A operand.
-//  * S^T puts one query per lane column, so the softmax row max/sum over keys
-//    is in-lane plus one permlane32 swap.  exp2 with log2(e) folded into the
-//    scale.
-//  * Split-KV: each split writes a normalised fp32 partial O and its base-2
-//    log-sum-exp; a second pass merges them (attn_merge_kernel).  The block
-//    rows are processed by the last split of each request.
+//  * S^T puts one query per lane column, so the softmax row max over keys is
+//    in-lane plus one permlane32 swap; exp2 with log2(e) folded into the
+//    scale; row sums of the bf16-rounded weights on the matrix cores.
+//  * Split-KV: each split writes its normalised partial O (in the path's
+//    dtype, in MFMA fragment order) and its base-2 log-sum-exp; a second
+//    launch merges them (attn_merge_kernel).  The block rows are processed by
+//    the last split of each request.
 //  * blockIdx.x = split * (B*Hkv) + (b*Hkv + g): with B*Hkv a multiple of 8
 //    every split of one KV head lands on the same XCD (work-groups are dealt
 //    round-robin over the 8 XCDs), sharing that XCD's L2 for the query tile.

@@ -167,23 +167,23 @@ attn_bf16_kernel(AttnParams p)
     const int64_t cont_base = ((int64_t)b * p.Hkv + g) * p.cap * D * 2;    // bytes
     const int64_t blk_base = ((int64_t)b * p.K * p.Hkv + g) * D * 2;
     const int blk_stride = p.Hkv * D * 2;
-    int lrow[LPT];                 // tile row loaded by this lane for load i
-    uint32_t loff[LPT];            // byte offset of the (swizzled) granule in the row
-    uint32_t ldst[LPT];            // LDS byte offset of the chunk within a slot
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-        const bool isv = i >= LK;
-        const int cc = (isv ? i - LK : i) * NW + wave;
-        if (!isv) {
-            lrow[i] = cc * RPCK + lane / GPR;
-            loff[i] = 16u * (uint32_t)((lane % GPR) ^ (lrow[i] & (GPR - 1)));
-            ldst[i] = cc * 1024;
-        } else {
-            lrow[i] = cc * RPCV + lane / GPRV;
-            loff[i] = 2u * col0 + 16u * (uint32_t)((lane % GPRV) ^ (2 * (lrow[i] & 3)));
-            ldst[i] = K_BYTES + cc * 1024;
-        }
-    }
+    // Load i of a tile by this lane (K chunks first, then V): the tile row it
+    // reads, the byte offset of its (swizzled) 16-byte granule in that row,
+    // and the LDS byte offset of its 1 KiB chunk within a ring slot.
+    // Recomputed where used (no per-lane arrays, which could land in scratch).
+    auto lrow = [&](int i) __attribute__((always_inline)) {
+        return i < LK ? (i * NW + wave) * RPCK + lane / GPR
+                      : ((i - LK) * NW + wave) * RPCV + lane / GPRV;
+    };
+    auto loff = [&](int i) __attribute__((always_inline)) -> uint32_t {
+        const int row = lrow(i);
+        return i < LK ? 16u * (uint32_t)((lane % GPR) ^ (row & (GPR - 1)))
+                      : 2u * col0 + 16u * (uint32_t)((lane % GPRV) ^ (2 * (row & 3)));
+    };
+    auto ldst = [&](int i) __attribute__((always_inline)) -> uint32_t {
+        return i < LK ? (uint32_t)((i * NW + wave) * 1024)
+                      : (uint32_t)(K_BYTES + ((i - LK) * NW + wave) * 1024);
+    };
 
     // Key range of this split: needs lens[b], which is read after the first
     // loads are in flight (contiguous layout: the split's nominal tiles are
@@ -194,7 +194,7 @@ attn_bf16_kernel(AttnParams p)
 
     // issue the global->LDS loads of tile t (rows start..start+count-1 of the
     // cache, or the block rows) into ring slot t % NSTAGE
-    auto issue_rows = [&](int t, bool is_blk, int start, int count) {
+    auto issue_rows = [&](int t, bool is_blk, int start, int count) __attribute__((always_inline)) {
         const uint32_t slot_lds = lds_base + (uint32_t)((t % NSTAGE) * SLOT);
         if (!is_blk && !PAGED && count == TK) {
             // fast path: a full contiguous tile, rows D*2 bytes apart
@@ -202,23 +202,23 @@ attn_bf16_kernel(AttnParams p)
             const char* vt = vc + cont_base + (int64_t)start * D * 2;
 #pragma unroll
             for (int i = 0; i < LPT; ++i)
-                lds_dma16((i >= LK ? vt : kt) + (uint32_t)(lrow[i] * D * 2) + loff[i],
-                          slot_lds + ldst[i]);
+                lds_dma16((i >= LK ? vt : kt) + (uint32_t)(lrow(i) * D * 2) + loff(i),
+                          slot_lds + ldst(i));
         } else if (!is_blk && PAGED && count == TK) {
             // full paged tile: 4 pages of 16 rows
             const int pidx = (start - kbeg) >> 4;
 #pragma unroll
             for (int i = 0; i < LPT; ++i) {
-                const int page = s_pages[pidx + (lrow[i] >> 4)];
+                const int page = s_pages[pidx + (lrow(i) >> 4)];
                 const char* base = (i >= LK ? vc : kc) + ((int64_t)page * p.Hkv + g) * (16 * D * 2);
-                lds_dma16(base + (uint32_t)((lrow[i] & 15) * D * 2) + loff[i], slot_lds + ldst[i]);
+                lds_dma16(base + (uint32_t)((lrow(i) & 15) * D * 2) + loff(i), slot_lds + ldst(i));
             }
         } else {
             // partial cache tile or the block tile: clamp rows to count-1
 #pragma unroll
             for (int i = 0; i < LPT; ++i) {
                 const bool isv = i >= LK;
-                const int rowc = lrow[i] < count ? lrow[i] : count - 1;
+                const int rowc = lrow(i) < count ? lrow(i) : count - 1;
                 const char* src;
                 if (is_blk) {
                     src = (isv ? (const char*)p.vb : (const char*)p.kb) + blk_base +
@@ -230,11 +230,11 @@ attn_bf16_kernel(AttnParams p)
                 } else {
                     src = (isv ? vc : kc) + cont_base + (int64_t)(start + rowc) * D * 2;
                 }
-                lds_dma16(src + loff[i], slot_lds + ldst[i]);
+                lds_dma16(src + loff(i), slot_lds + ldst(i));
             }
         }
     };
-    auto issue = [&](int t) {
+    auto issue = [&](int t) __attribute__((always_inline)) {
         const bool is_blk = t >= n_cache_tiles;
         const int start = is_blk ? 0 : kbeg + t * TK;
         const int count = is_blk ? p.K : (kend - start < TK ? kend - start : TK);
@@ -243,7 +243,7 @@ attn_bf16_kernel(AttnParams p)
     };
 
     // wait until at most `pending` later tiles of this lane are in flight
-    auto wait_tiles = [&](int pending) {
+    auto wait_tiles = [&](int pending) __attribute__((always_inline)) {
         switch (pending) {
             case 0: __builtin_amdgcn_s_waitcnt(vmcnt_encode(0)); break;
             case 1: __builtin_amdgcn_s_waitcnt(vmcnt_encode(LPT)); break;
@@ -332,7 +332,7 @@ attn_bf16_kernel(AttnParams p)
     // whose operands are then in registers, so the refill (tile t + NPRE)
     // may take the slot of tile t-1 (NSTAGE = NPRE + 1).
     static_assert(NSTAGE >= NPRE + 1, "ring slots for the tiles in flight");
-    auto arrive = [&](int t) {
+    auto arrive = [&](int t) __attribute__((always_inline)) {
         wait_tiles(last_issued - t);
         __syncthreads();
         if (t + NPRE < n_tiles) issue(t + NPRE);
@@ -460,7 +460,7 @@ attn_bf16_kernel(AttnParams p)
     // takes the other slice's accumulators for its own half.
     constexpr int HALF_DT = KS > 1 ? NDT / 2 : NDT;
     // does this wave write D tile dt of the result?
-    auto owns = [&](int dt) { return KS == 1 || ((dt < HALF_DT) == (kg == 0)); };
+    auto owns = [&](int dt) __attribute__((always_inline)) { return KS == 1 || ((dt < HALF_DT) == (kg == 0)); };
     if constexpr (KS > 1) {
         static_assert(KS == 2 && NDT % 2 == 0, "two key slices, even number of D tiles");
         constexpr int REC = HALF_DT * 16 + 4;             // floats per lane record
@@ -470,7 +470,7 @@ attn_bf16_kernel(AttnParams p)
         float* base = reinterpret_cast<float*>(smem) + rg * 2 * 64 * REC;
         float* mine = base + (kg * 64 + lane) * REC;
         const float* other = base + ((1 - kg) * 64 + lane) * REC;
-        auto put = [&](int dt0) {
+        auto put = [&](int dt0) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < HALF_DT; ++j)
 #pragma unroll
@@ -487,7 +487,7 @@ attn_bf16_kernel(AttnParams p)
         const float m_t = fmaxf(m_run, m_o);
         const float a0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_t) * c);
         const float a1 = (m_o == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_o - m_t) * c);
-        auto take = [&](int dt0) {
+        auto take = [&](int dt0) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < HALF_DT; ++j)
 #pragma unroll

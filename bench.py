@@ -10,6 +10,12 @@ Every layer has its own synthetic cache (1.2 GB in total, resident in HBM).
 The step is captured in a HIP graph; W warm-up replays, then K timed replays
 between two synchronisations.  Prints ONE JSON line.
 
+--config N runs another workload (1 tiny fp32, 2 Qwen3-1.7B layer, 4 paged
+serving, 5 long context with --K in {4, 8, 16, 32, 64}).  A workload whose
+inputs span less than 512 MiB cycles that many copies of them (one per
+consecutive step, each replay runs all of them), so that no step is served
+from the 256 MB last-level cache; "steps" then counts the steps timed.
+
 The oracle (fp64 CPU) is timed on the host cores on a bounded sample of the
 same step ("cpu_baseline"); it is a reported baseline, not the target.
 """
@@ -68,6 +74,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets cycled by consecutive steps (0 = enough for 512 MiB)")
     ap.add_argument("--calib-bytes", type=int, default=0,
                     help="first run one plain device copy of this many bytes (a known-size "
                          "kernel for scaling hardware byte counters)")
@@ -81,7 +89,7 @@ def log(*a):
 class Step:
     """Device-resident inputs and outputs of one decode step of a workload."""
 
-    def __init__(self, cfg, splits, dev="cuda"):
+    def __init__(self, cfg, splits, sets=0, dev="cuda"):
         import torch
         import workloads as W
         from ar_shared_kv_amd import api
@@ -89,15 +97,29 @@ class Step:
         self.splits = splits
         nl = cfg.layers
         st = W.step_inputs(cfg, layers=1, with_logits=True)   # shapes + logits + lens
+        # Input sets cycled by consecutive steps, so that a small workload's
+        # inputs are not served from the 256 MB last-level cache: enough
+        # copies of the step's inputs to span 512 MiB.
+        e = 2 if cfg.dtype == "bf16" else 4
+        lay0 = st.layers[0]
+        per_set = nl * e * sum(getattr(lay0, k).numel() for k in
+                               ("k_cache", "v_cache", "q_diff", "q_ar", "k_blk_diff",
+                                "v_blk_diff", "k_blk_ar", "v_blk_ar"))
+        per_set += e * (st.diff_logits.numel() + st.ar_logits.numel())
+        if sets <= 0:
+            sets = min(64, max(1, -(-(512 << 20) // per_set)))
+        self.sets = sets
+        self.set_bytes = per_set
+        nt = nl * sets
         self.lens = st.lens.to(dev)
         self.lens_out = torch.empty_like(self.lens)
         self.page_table = st.page_table.to(dev) if cfg.paged else None
         cshape = tuple(st.layers[0].k_cache.shape)
         dt = cfg.torch_dtype
-        self.kc = torch.empty((nl, *cshape), dtype=dt, device=dev)
+        self.kc = torch.empty((nt, *cshape), dtype=dt, device=dev)
         self.vc = torch.empty_like(self.kc)
-        qs = (nl, cfg.B, cfg.K, cfg.Hq, cfg.D)
-        bs = (nl, cfg.B, cfg.K, cfg.Hkv, cfg.D)
+        qs = (nt, cfg.B, cfg.K, cfg.Hq, cfg.D)
+        bs = (nt, cfg.B, cfg.K, cfg.Hkv, cfg.D)
         self.q = {v: torch.empty(qs, dtype=dt, device=dev) for v in ("diff", "ar")}
         self.kb = {v: torch.empty(bs, dtype=dt, device=dev) for v in ("diff", "ar")}
         self.vb = {v: torch.empty(bs, dtype=dt, device=dev) for v in ("diff", "ar")}
@@ -111,14 +133,19 @@ class Step:
                 self.q[v][l].copy_(getattr(lay, f"q_{v}"))
                 self.kb[v][l].copy_(getattr(lay, f"k_blk_{v}"))
                 self.vb[v][l].copy_(getattr(lay, f"v_blk_{v}"))
-        log(f"inputs for {nl} layers generated in {time.time() - t0:.1f}s")
+        for x in [self.kc, self.vc] + [d[v] for d in (self.q, self.kb, self.vb)
+                                       for v in ("diff", "ar")]:
+            for si in range(1, sets):   # copies: other addresses, same values
+                x[si * nl:(si + 1) * nl].copy_(x[:nl])
+        log(f"inputs for {nl} layers x {sets} input sets generated in {time.time() - t0:.1f}s")
         self.step_inputs = st
-        self.diff_logits = st.diff_logits.to(dev)
-        self.ar_logits = st.ar_logits.to(dev)
+        dl, al = st.diff_logits.to(dev), st.ar_logits.to(dev)
+        self.diff_logits = [dl] + [dl.clone() for _ in range(1, sets)]
+        self.ar_logits = [al] + [al.clone() for _ in range(1, sets)]
         lmax = int(st.lens.max())
         self.caches = [api.make_cache(self.kc[l], self.vc[l], self.lens,
                                       page_table=self.page_table, max_len=lmax)
-                       for l in range(nl)]
+                       for l in range(nt)]
         self.out = torch.empty(qs[1:], dtype=dt, device=dev)
         self.lse = torch.empty((cfg.B, cfg.Hq, cfg.K), dtype=torch.float32, device=dev)
         dcode = api.dtype_code(self.q["ar"])
@@ -134,19 +161,28 @@ class Step:
                        self.caches[layer], mask=mask, scale=self.cfg.scale,
                        num_splits=self.splits, out=self.out, lse=self.lse, workspace=self.ws)
 
-    def attention_passes(self):
+    def attention_set(self, si):
+        nl = self.cfg.layers
         for view in ("diff", "ar"):          # all diffusion layers, then all AR layers
-            for l in range(self.cfg.layers):
-                self.attention(view, l)
+            for l in range(nl):
+                self.attention(view, si * nl + l)
+
+    def attention_passes(self):
+        """Block attention of `sets` consecutive steps."""
+        for si in range(self.sets):
+            self.attention_set(si)
 
     def run(self):
+        """`sets` consecutive decode steps, one per input set."""
         from ar_shared_kv_amd import api
-        self.attention_passes()
-        api.consensus(self.diff_logits, self.ar_logits, self.cbufs)
-        api.kv_append(self.caches[0], self.kb["ar"][0], self.vb["ar"][0], self.cbufs.n_emit,
-                      self.lens_out, num_layers=self.cfg.layers,
-                      cache_layer_stride=self.kc[0].numel(),
-                      blk_layer_stride=self.kb["ar"][0].numel())
+        nl = self.cfg.layers
+        for si in range(self.sets):
+            self.attention_set(si)
+            api.consensus(self.diff_logits[si], self.ar_logits[si], self.cbufs)
+            api.kv_append(self.caches[si * nl], self.kb["ar"][si * nl], self.vb["ar"][si * nl],
+                          self.cbufs.n_emit, self.lens_out, num_layers=nl,
+                          cache_layer_stride=self.kc[0].numel(),
+                          blk_layer_stride=self.kb["ar"][0].numel())
 
     # algorithmic bytes (see DESIGN.md): inputs read once + outputs written once
     def attn_bytes_per_launch(self):
@@ -269,13 +305,14 @@ def main():
         torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    step = Step(cfg, splits)
+    step = Step(cfg, splits, args.sets)
     graph = not args.no_graph
 
-    ms_step, _ = timed(step.run, args.steps, args.warmup, graph)
-    # the dominant kernel: block attention alone, all 2*layers passes per replay
+    ms_run, _ = timed(step.run, args.steps, args.warmup, graph)
+    ms_step = ms_run / step.sets
+    # the dominant kernel: block attention alone, all 2*layers passes per step
     ms_attn_all, _ = timed(step.attention_passes, args.steps, args.warmup, graph)
-    us_attn = ms_attn_all * 1e3 / (2 * cfg.layers)
+    us_attn = ms_attn_all * 1e3 / (2 * cfg.layers * step.sets)
     n = step.cbufs.n_emit.cpu()
     n_total = int(n.sum())
 
@@ -288,8 +325,8 @@ def main():
         "value": round(steps_s, 3),
         "unit": "steps/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": args.steps * step.sets,
+        "warmup": args.warmup * step.sets,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -299,10 +336,10 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
                    "K": cfg.K, "L": cfg.L if cfg.L_range is None else list(cfg.L_range),
                    "layers": cfg.layers, "V": cfg.V, "paged": cfg.paged,
-                   "num_splits": splits or "auto", "graph": graph},
+                   "num_splits": splits or "auto", "graph": graph, "input_sets": step.sets},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(cfg.name, args.splits),
+                     "traffic": None if args.K else measured_traffic(cfg.name, args.splits),
                      "kernel": "block attention (attn_bf16_kernel + split merge), per launch",
                      "us_per_launch": round(us_attn, 3), "bytes_per_launch": attn_b,
                      "mfma_frac": round(attn_f / (us_attn * 1e-6) / 2.5e15, 4)},

@@ -309,20 +309,28 @@ attn_bf16_kernel(AttnParams p)
     // Tile t's scores: S^T = K Q^T for this wave's key slice of ring slot t.
     auto qk = [&](int t, f32x16 (&sacc)[NBLK]) {
         const char* Ks = smem + (t % NSTAGE) * SLOT;
+        // operand reads first, then the MFMAs; with two 32-key blocks per wave
+        // (64 keys) in halves of D, to stay within the register budget
+        constexpr int KCH = NBLK > 1 ? 2 : 1;
+        constexpr int DSC = D / 16 / KCH;
 #pragma unroll
         for (int kb = 0; kb < NBLK; ++kb) {
             const int krow = kg * KPW + kb * 32 + (lane & 31);
-            u32x4 kf[D / 16];   // all operand reads of the block first, then the MFMAs
-#pragma unroll
-            for (int ds = 0; ds < D / 16; ++ds) {
-                const int lgr = (2 * ds + half) ^ (krow & (GPR - 1));
-                kf[ds] = *(const u32x4*)(Ks + krow * D * 2 + lgr * 16);
-            }
             sacc[kb] = f32x16{};
 #pragma unroll
-            for (int ds = 0; ds < D / 16; ++ds)
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, kf[ds]), qreg[ds], sacc[kb], 0, 0, 0);
+            for (int ch = 0; ch < KCH; ++ch) {
+                u32x4 kf[DSC];
+#pragma unroll
+                for (int j = 0; j < DSC; ++j) {
+                    const int ds = ch * DSC + j;
+                    const int lgr = (2 * ds + half) ^ (krow & (GPR - 1));
+                    kf[j] = *(const u32x4*)(Ks + krow * D * 2 + lgr * 16);
+                }
+#pragma unroll
+                for (int j = 0; j < DSC; ++j)
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, kf[j]), qreg[ch * DSC + j], sacc[kb], 0, 0, 0);
+            }
         }
     };
     // wait for this lane's loads of tile t (and, for t = 0, the query tile
@@ -505,7 +513,10 @@ attn_bf16_kernel(AttnParams p)
 
     // ---- finalize: lane owns query row r, columns col0 + 32dt + 8(i/4) + 4*half + i%4 ----
     const float inv = 1.f / l_run;
-    if (p.S_grid > 1) {
+    // Paged batches are ragged: a request with a single split writes its rows
+    // directly (the merge skips it).  Contiguous launches keep one epilogue
+    // per grid (measured faster at the benchmark shape).
+    if (PAGED ? S_b > 1 : p.S_grid > 1) {
         // split partial, stored in fragment order: each store is 512
         // contiguous bytes per wave; base-2 lse per row
         // row groups past Mpad (M not a multiple of the row block) hold no rows
@@ -527,8 +538,9 @@ attn_bf16_kernel(AttnParams p)
         }
         return;
     }
-    // One split: stage the rows in LDS ([row][DC] with a 16-byte pad) so that
-    // the output stores are whole 16-byte pieces of rows.
+    // No merge for these rows: stage them in
+    // LDS ([row][DC] with a 16-byte pad) so that the output stores are whole
+    // 16-byte pieces of rows.
     constexpr int RSTR = DC * 2 + 16;                       // staged row stride, bytes
     static_assert(QROWS * RSTR <= NSTAGE * SLOT, "staging buffer");
     __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));
@@ -693,7 +705,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams p)
         const int h = g * p.G + hl;
         const float inv = 1.f / l_run[j];
         const float lse2 = m_run[j] * c + log2f(l_run[j]);
-        if (p.S_grid == 1) {
+        if (p.layout == 1 ? S_b == 1 : p.S_grid == 1) {   // no merge for these rows
             float* op = (float*)p.out + (((int64_t)b * p.K + qi) * p.Hq + h) * D;
 #pragma unroll
             for (int k = 0; k < DC; ++k) op[lane + 64 * k] = o[j][k] * inv;
@@ -715,10 +727,13 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams p)
 // of 128 threads covers 32 rows x 16 columns: thread = (row q, 4 columns), so
 // 32 consecutive threads read one contiguous run of a partial block (and of
 // the lse); each thread issues the loads of up to UNROLL splits at once.
-template <int D, bool BF16>
+// UNROLL: splits loaded per round (the launch picks about the grid's split
+// count, so that few loads are redundant).
+// SKIP1: paged launches, whose single-split requests were written by the
+// attention kernel itself.
+template <int D, bool BF16, int UNROLL, bool SKIP1>
 __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
 {
-    constexpr int UNROLL = BF16 ? 32 : 16;
     const int bh = blockIdx.x;
     const int b = bh / p.Hkv;
     const int g = bh % p.Hkv;
@@ -742,7 +757,8 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
     };
     f32x4 v[UNROLL];
     float l2[UNROLL];
-    auto load = [&](int s0) {   // splits s0.. (clamped into the grid)
+    auto load = [&](int s0) {   // splits s0.. (clamped into the grid; no branches,
+                                // so that all loads are in flight together)
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int sp = s0 + u < p.S_grid ? s0 + u : p.S_grid - 1;
@@ -758,6 +774,7 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
     const int L = ((const __attribute__((address_space(4))) int32_t*)p.lens)[b];
     int S_b = (L + p.SL - 1) / p.SL;
     S_b = S_b < 1 ? 1 : (S_b > p.S_grid ? p.S_grid : S_b);
+    if (SKIP1 && S_b == 1) return;
     float mx = -INFINITY;
     float W = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -839,6 +856,24 @@ static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int D, bool BF16, bool SKIP1>
+static void launch_merge_u(const AttnParams& p, dim3 grid, hipStream_t st) {
+    if (p.S_grid <= 4)
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 4, SKIP1>), grid, dim3(128), 0, st, p);
+    else if (p.S_grid <= 8)
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 8, SKIP1>), grid, dim3(128), 0, st, p);
+    else if (p.S_grid <= 16 || !BF16)
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 16, SKIP1>), grid, dim3(128), 0, st, p);
+    else
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 32, SKIP1>), grid, dim3(128), 0, st, p);
+}
+
+template <int D, bool BF16>
+static void launch_merge(const AttnParams& p, dim3 grid, hipStream_t st) {
+    if (p.layout == 1) launch_merge_u<D, BF16, true>(p, grid, st);
+    else launch_merge_u<D, BF16, false>(p, grid, st);
+}
+
 template <int D>
 static hipError_t launch_bf16_d(const AttnParams& p, hipStream_t st) {
     switch (p.rows_per_wg) {
@@ -870,11 +905,11 @@ hipError_t launch_block_attn(const AttnParams& p, int dtype, hipStream_t st) {
     if (e != hipSuccess || p.S_grid == 1) return e;
     dim3 mgrid(p.B * p.Hkv, (p.Mpad / 32) * (p.D / 16));
     if (p.D == 128) {
-        if (dtype == 1) hipLaunchKernelGGL((attn_merge_kernel<128, true>), mgrid, dim3(128), 0, st, p);
-        else hipLaunchKernelGGL((attn_merge_kernel<128, false>), mgrid, dim3(128), 0, st, p);
+        if (dtype == 1) launch_merge<128, true>(p, mgrid, st);
+        else launch_merge<128, false>(p, mgrid, st);
     } else {
-        if (dtype == 1) hipLaunchKernelGGL((attn_merge_kernel<64, true>), mgrid, dim3(128), 0, st, p);
-        else hipLaunchKernelGGL((attn_merge_kernel<64, false>), mgrid, dim3(128), 0, st, p);
+        if (dtype == 1) launch_merge<64, true>(p, mgrid, st);
+        else launch_merge<64, false>(p, mgrid, st);
     }
     return hipGetLastError();
 }

@@ -14,7 +14,8 @@ namespace {
 
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 constexpr int kTargetWorkGroups = 256;    // one attention work-group per CU on MI355X
-constexpr int kMinKeysPerSplit = 256;
+constexpr int kMinKeysPerSplit = 256;     // bf16 (MFMA) path
+constexpr int kMinKeysPerSplitF32 = 64;   // fp32 (vector ALU) path: compute-bound per tile
 constexpr int64_t kMaxGrid = 2147483647;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -72,7 +73,8 @@ AttnPlan plan_block_attn(const orthrus_cache *c, int B, int K, int Hq, int Hkv, 
         S = num_splits;
     } else {
         S = ceil_div(kTargetWorkGroups, (int64_t)B * Hkv * pl.row_blocks * pl.ds);
-        const int64_t cap_s = ceil_div(lmax, kMinKeysPerSplit);
+        const int64_t cap_s =
+            ceil_div(lmax, dtype == ORTHRUS_F32 ? kMinKeysPerSplitF32 : kMinKeysPerSplit);
         if (S > cap_s) S = cap_s;
     }
     if (S < 1) S = 1;

@@ -588,8 +588,8 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams p)
     constexpr int DC = D / 64;            // output columns per lane
     __shared__ float Ks[TK][D + 1];
     __shared__ float Vs[TK][D];
-    __shared__ float Qs[ROWS][D];
-    __shared__ float Ps[4][TK];
+    __shared__ __attribute__((aligned(16))) float Qs[ROWS][D];
+    __shared__ __attribute__((aligned(16))) float Ps[4][RW][TK];   // per wave: the rows' weights of a tile
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -633,12 +633,17 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams p)
         for (int k = 0; k < DC; ++k) o[j][k] = 0.f;
     }
     const float c = p.c;
-    for (int t = 0; t < n_tiles; ++t) {
+    // tile t's K/V values of this thread (element i = tid + 256*e of the
+    // 64 x D tile), loaded into registers one tile ahead of the compute
+    constexpr int E = TK * D / 256;
+    float kr[E], vr[E];
+    auto load_tile = [&](int t) __attribute__((always_inline)) {
         const bool is_blk = t >= n_cache_tiles;
         const int start = is_blk ? 0 : kbeg + t * TK;
         const int count = is_blk ? p.K : (kend - start < TK ? kend - start : TK);
-        __syncthreads();
-        for (int i = tid; i < TK * D; i += 256) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = tid + 256 * e;
             const int row = i / D, d = i % D;
             float kv = 0.f, vv = 0.f;
             if (row < count) {
@@ -659,43 +664,88 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams p)
                     vv = vc[off];
                 }
             }
-            Ks[row][d] = kv;
-            Vs[row][d] = vv;
+            kr[e] = kv;
+            vr[e] = vv;
         }
+    };
+    load_tile(0);
+    for (int t = 0; t < n_tiles; ++t) {
+        const bool is_blk = t >= n_cache_tiles;
+        const int start = is_blk ? 0 : kbeg + t * TK;
+        const int count = is_blk ? p.K : (kend - start < TK ? kend - start : TK);
+        __syncthreads();   // the previous tile's reads of Ks/Vs are done
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = tid + 256 * e;
+            Ks[i / D][i % D] = kr[e];
+            Vs[i / D][i % D] = vr[e];
+        }
+        if (t + 1 < n_tiles) load_tile(t + 1);   // in flight during this tile's compute
         __syncthreads();
+        // scores of the wave's RW rows against key `lane`: one K read feeds
+        // RW FMAs, the query values come as broadcast float4 reads
+        float sc[RW];
+#pragma unroll
+        for (int j = 0; j < RW; ++j) sc[j] = 0.f;
+#pragma unroll 4
+        for (int d = 0; d < D; d += 4) {
+            const float k0 = Ks[lane][d], k1 = Ks[lane][d + 1], k2 = Ks[lane][d + 2],
+                        k3 = Ks[lane][d + 3];
+#pragma unroll
+            for (int j = 0; j < RW; ++j) {
+                const f32x4 qv = *(const f32x4*)&Qs[wave * RW + j][d];
+                sc[j] = __builtin_fmaf(qv[0], k0, sc[j]);
+                sc[j] = __builtin_fmaf(qv[1], k1, sc[j]);
+                sc[j] = __builtin_fmaf(qv[2], k2, sc[j]);
+                sc[j] = __builtin_fmaf(qv[3], k3, sc[j]);
+            }
+        }
+        float corr[RW];
 #pragma unroll
         for (int j = 0; j < RW; ++j) {
-            const int lr = wave * RW + j;
-            const int rr = row0 + lr;
+            const int rr = row0 + wave * RW + j;
             const int qi = rr < p.M ? rr % p.K : 0;
-            float sc = 0.f;
-#pragma unroll 8
-            for (int d = 0; d < D; ++d) sc = __builtin_fmaf(Qs[lr][d], Ks[lane][d], sc);
             bool ok = lane < count;
             if (is_blk && p.mask == 1) ok = ok && lane <= qi;
-            sc = ok ? sc : -INFINITY;
-            float mx = sc;
+            const float sj = ok ? sc[j] : -INFINITY;
+            float mx = sj;
 #pragma unroll
             for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
             const float m_new = fmaxf(m_run[j], mx);
-            const float corr = (m_run[j] == -INFINITY) ? 0.f : exp2f((m_run[j] - m_new) * c);
-            const float pv = ok ? exp2f((sc - m_new) * c) : 0.f;
+            corr[j] = (m_run[j] == -INFINITY) ? 0.f : exp2f((m_run[j] - m_new) * c);
+            const float pv = ok ? exp2f((sj - m_new) * c) : 0.f;
             m_run[j] = m_new;
             float ps = pv;
 #pragma unroll
             for (int m = 32; m >= 1; m >>= 1) ps += __shfl_xor(ps, m, 64);
-            l_run[j] = l_run[j] * corr + ps;
-            Ps[wave][lane] = pv;
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int k = 0; k < DC; ++k) {
-                float acc = o[j][k] * corr;
-                for (int key = 0; key < TK; ++key)
-                    acc = __builtin_fmaf(Ps[wave][key], Vs[key][lane + 64 * k], acc);
-                o[j][k] = acc;
-            }
-            __builtin_amdgcn_wave_barrier();
+            l_run[j] = l_run[j] * corr[j] + ps;
+            Ps[wave][j][lane] = pv;
         }
+        __builtin_amdgcn_wave_barrier();
+        // O += P V: one V read feeds RW FMAs, the weights come as broadcast
+        // float4 reads
+#pragma unroll
+        for (int k = 0; k < DC; ++k) {
+            float acc[RW];
+#pragma unroll
+            for (int j = 0; j < RW; ++j) acc[j] = o[j][k] * corr[j];
+#pragma unroll 4
+            for (int key = 0; key < TK; key += 4) {
+                const float v0 = Vs[key][lane + 64 * k], v1 = Vs[key + 1][lane + 64 * k],
+                            v2 = Vs[key + 2][lane + 64 * k], v3 = Vs[key + 3][lane + 64 * k];
+#pragma unroll
+                for (int j = 0; j < RW; ++j) {
+                    const f32x4 pw = *(const f32x4*)&Ps[wave][j][key];
+                    acc[j] = __builtin_fmaf(pw[0], v0, acc[j]);
+                    acc[j] = __builtin_fmaf(pw[1], v1, acc[j]);
+                    acc[j] = __builtin_fmaf(pw[2], v2, acc[j]);
+                    acc[j] = __builtin_fmaf(pw[3], v3, acc[j]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < RW; ++j) o[j][k] = acc[j];
+        }
+        __builtin_amdgcn_wave_barrier();
     }
 #pragma unroll
     for (int j = 0; j < RW; ++j) {

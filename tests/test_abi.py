@@ -83,9 +83,15 @@ def test_block_attn_workspace_formula():
     assert n == -(-rows * 128 * 2 // 256) * 256 + rows * 4
     nf = B.orthrus_block_attn_workspace_bytes(c, 1, 64, 32, 8, 128, B.F32, 64)
     assert nf == -(-rows * 128 * 4 // 256) * 256 + rows * 4
-    # one split -> no workspace
-    small = cache(capacity=128, max_len=128)
+    # one split -> no workspace (fp32 splits go down to 64 keys, bf16 to 256)
+    small = cache(capacity=128, max_len=64)
     assert B.orthrus_block_attn_workspace_bytes(small, 1, 8, 2, 1, 64, B.F32, 0) == 0
+    assert B.orthrus_block_attn_workspace_bytes(small, 1, 8, 2, 1, 64, B.BF16, 0) == 0
+    # 128 keys in fp32: two splits of 64; M = 16 rows padded to 32
+    small = cache(capacity=128, max_len=128)
+    rows = 1 * 1 * 2 * 32
+    assert B.orthrus_block_attn_workspace_bytes(small, 1, 8, 2, 1, 64, B.F32, 0) == \
+        rows * 64 * 4 + rows * 4
     assert B.orthrus_block_attn_workspace_bytes(c, 1, 64, 32, 8, 96, B.BF16, 0) == 0   # invalid
 
 

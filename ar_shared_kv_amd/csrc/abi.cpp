@@ -14,7 +14,7 @@ namespace {
 
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 constexpr int kTargetWorkGroups = 256;    // one attention work-group per CU on MI355X
-constexpr int kMinKeysPerSplit = 256;     // bf16 (MFMA) path
+constexpr int kMinKeysPerSplit = 128;     // bf16 (MFMA) path: two tiles per split at least
 constexpr int kMinKeysPerSplitF32 = 64;   // fp32 (vector ALU) path: compute-bound per tile
 constexpr int64_t kMaxGrid = 2147483647;
 

@@ -92,3 +92,25 @@ def test_batched_ragged_acceptance():
     diff, ar = W.consensus_logits(cfg.B, cfg.K, 4096, ps, torch.bfloat16, 4242)
     r = check_consensus(diff, ar, "ragged batch")
     assert len(set(r["n"].tolist())) > 3
+
+
+@pytest.mark.parametrize("B,K", [(1, 64), (16, 32), (65, 8), (300, 4), (1100, 2), (4000, 16)],
+                         ids=["B1-K64", "B16", "B65", "B300", "B1100-two-level", "B4000"])
+def test_batch_sizes_cover_every_scan_path(B, K):
+    # small batches keep tokens in LDS; more than 64 requests use the
+    # work-group scan, more than 1024 give each thread a run of requests
+    V = 600
+    ps = torch.linspace(0.3, 0.97, B).tolist()
+    diff, ar = W.consensus_logits(B, K, V, ps, torch.bfloat16, 777 + B)
+    r = check_consensus(diff, ar, f"B={B} K={K}")
+    assert r["emit_off"][-1] == int(r["n"].sum())
+
+
+def test_argmax_many_rows_and_chunks():
+    # rows not a multiple of the 16 rows a work-group reduces; > 64 chunks per row
+    x = torch.randn(41, 600000).to(torch.bfloat16)
+    x[5, 599999] = 50.0
+    x[40, 0] = 50.0
+    idx = api.argmax(dev(x))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.argmax_rows(f64(x)))

@@ -24,7 +24,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct AttnPlan {
     int status;
-    int M, G, rows_per_wg, row_blocks, SL, S_grid, ds;
+    int M, G, rows_per_wg, row_blocks, SL, S_grid;
     size_t ws_bytes, ws_lse_offset;
 };
 
@@ -63,16 +63,11 @@ AttnPlan plan_block_attn(const orthrus_cache *c, int B, int K, int Hq, int Hkv, 
     pl.M = pl.G * K;
     pl.rows_per_wg = attn_rows_per_wg(dtype, pl.M);
     pl.row_blocks = (int)ceil_div(pl.M, pl.rows_per_wg);
-    // Output-column split: with bf16, D = 128 and 128 query rows per work-group,
-    // two work-groups share a key range (each loads K, and half of V), which
-    // halves the number of key splits, and so the split partials, for the same
-    // number of work-groups.  Only with the automatic split plan.
-    pl.ds = 1;
     int64_t S;
     if (num_splits > 0) {
         S = num_splits;
     } else {
-        S = ceil_div(kTargetWorkGroups, (int64_t)B * Hkv * pl.row_blocks * pl.ds);
+        S = ceil_div(kTargetWorkGroups, (int64_t)B * Hkv * pl.row_blocks);
         const int64_t cap_s =
             ceil_div(lmax, dtype == ORTHRUS_F32 ? kMinKeysPerSplitF32 : kMinKeysPerSplit);
         if (S > cap_s) S = cap_s;
@@ -90,7 +85,7 @@ AttnPlan plan_block_attn(const orthrus_cache *c, int B, int K, int Hq, int Hkv, 
         S_grid = ceil_div(c->max_pages_per_req * (int64_t)c->page_size, SL);
     }
     if (S_grid < 1) S_grid = 1;
-    if ((int64_t)B * Hkv * S_grid > kMaxGrid || (int64_t)pl.row_blocks * pl.ds > 65535) {
+    if ((int64_t)B * Hkv * S_grid > kMaxGrid || pl.row_blocks > 65535) {
         pl.status = ORTHRUS_ERR_UNSUPPORTED;
         return pl;
     }
@@ -184,7 +179,6 @@ int orthrus_block_attn(const orthrus_cache *cache, const void *q, const void *k_
     p.S_grid = pl.S_grid;
     p.rows_per_wg = pl.rows_per_wg;
     p.row_blocks = pl.row_blocks;
-    p.ds = pl.ds;
     p.c = scale * 1.4426950408889634f;
     if (pl.S_grid > 1) {
         p.ws_o = workspace;

@@ -60,29 +60,27 @@ __device__ __forceinline__ int64_t frag_offset(int r, int d, int D) {
 // bf16 MFMA kernel
 // --------------------------------------------------------------------------
 // NR: 32-row query groups per work-group; KS: waves sharing one row group,
-// each taking a 64/KS-key slice of every tile (waves = NR*KS); DS: the output
-// columns are split over DS work-groups (each loads all of K for the scores
-// but only its D/DS columns of V); NSTAGE: ring slots; NPRE: tiles kept in
+// each taking a 64/KS-key slice of every tile (waves = NR*KS); NSTAGE: ring
+// slots; NPRE: tiles kept in
 // flight ahead of the one being computed; QLDS: the query tile is fetched by
 // LDS DMA as part of the prologue instead of through VGPR loads.
-template <int D, int NR, int KS, int DS, int NSTAGE, int NPRE, bool PAGED, bool QLDS>
+template <int D, int NR, int KS, int NSTAGE, int NPRE, bool PAGED, bool QLDS>
 __global__ void __launch_bounds__(64 * NR * KS)
 attn_bf16_kernel(AttnParams p)
 {
     constexpr int NW = NR * KS;
-    constexpr int DC = D / DS;                 // output columns of this work-group
     constexpr int GPR = D / 8;                 // 16-byte granules per K row
-    constexpr int GPRV = DC / 8;               // 16-byte granules per V row slice
+    constexpr int GPRV = D / 8;                // 16-byte granules per V row
     constexpr int RPCK = 64 / GPR;             // K rows per 1 KiB chunk
     constexpr int RPCV = 64 / GPRV;            // V rows per 1 KiB chunk
     constexpr int CK = TK / RPCK;              // K chunks per tile
     constexpr int CV = TK / RPCV;              // V chunks per tile
     constexpr int K_BYTES = TK * D * 2;
-    constexpr int V_BYTES = TK * DC * 2;
+    constexpr int V_BYTES = TK * D * 2;
     constexpr int SLOT = K_BYTES + V_BYTES;
     constexpr int KPW = TK / KS;               // keys per wave per tile
     constexpr int NBLK = KPW / 32;             // S^T 32x32 blocks per wave
-    constexpr int NDT = DC / 32;               // O^T tiles
+    constexpr int NDT = D / 32;                // O^T tiles
     constexpr int QROWS = 32 * NR;
     constexpr int Q_BYTES = QLDS ? QROWS * D * 2 : 0;
     constexpr int CQ = Q_BYTES / 1024;         // query chunks
@@ -116,9 +114,7 @@ attn_bf16_kernel(AttnParams p)
     const int s = blockIdx.x / BH;
     const int b = bh / p.Hkv;
     const int g = bh % p.Hkv;
-    const int rb = blockIdx.y / DS;   // row block
-    const int dh = blockIdx.y % DS;   // column slice
-    const int col0 = dh * DC;
+    const int rb = blockIdx.y;        // row block
     const int kbeg = s * p.SL;
 
     // ---- query rows: lane column q = lane % 32 of row group rg ----
@@ -178,7 +174,7 @@ attn_bf16_kernel(AttnParams p)
     auto loff = [&](int i) __attribute__((always_inline)) -> uint32_t {
         const int row = lrow(i);
         return i < LK ? 16u * (uint32_t)((lane % GPR) ^ (row & (GPR - 1)))
-                      : 2u * col0 + 16u * (uint32_t)((lane % GPRV) ^ (2 * (row & 3)));
+                      : 16u * (uint32_t)((lane % GPRV) ^ (2 * (row & 3)));
     };
     auto ldst = [&](int i) __attribute__((always_inline)) -> uint32_t {
         return i < LK ? (uint32_t)((i * NW + wave) * 1024)
@@ -440,7 +436,7 @@ attn_bf16_kernel(AttnParams p)
                     for (int ins = 0; ins < 2; ++ins) {
                         const int row = rowbase + 8 * ins;
                         const int gr = (col >> 3) ^ (2 * (row & 3));
-                        const uint16_t* a = Vs + row * DC + gr * 8 + (col & 7);
+                        const uint16_t* a = Vs + row * D + gr * 8 + (col & 7);
                         vv[ins] = __builtin_bit_cast(
                             u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((ORTHRUS_LDS s16x4*)a));
                     }
@@ -511,7 +507,7 @@ attn_bf16_kernel(AttnParams p)
         m_run = m_t;
     }
 
-    // ---- finalize: lane owns query row r, columns col0 + 32dt + 8(i/4) + 4*half + i%4 ----
+    // ---- finalize: lane owns query row r, columns 32dt + 8(i/4) + 4*half + i%4 ----
     const float inv = 1.f / l_run;
     // Paged batches are ragged: a request with a single split writes its rows
     // directly (the merge skips it).  Contiguous launches keep one epilogue
@@ -528,20 +524,20 @@ attn_bf16_kernel(AttnParams p)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int i0 = 4 * q4;
-                    const int64_t off = frag_offset(r, col0 + 32 * dt + 8 * q4 + 4 * half, D);
+                    const int64_t off = frag_offset(r, 32 * dt + 8 * q4 + 4 * half, D);
                     *(u32x2*)(blk + off) =
                         u32x2{pack_bf16x2(oacc[dt][i0] * inv, oacc[dt][i0 + 1] * inv),
                               pack_bf16x2(oacc[dt][i0 + 2] * inv, oacc[dt][i0 + 3] * inv)};
                 }
-            if (row_ok && half == 0 && dh == 0 && kg == 0)
+            if (row_ok && half == 0 && kg == 0)
                 p.ws_lse[((int64_t)bh * p.S_grid + s) * p.Mpad + r] = m_run * c + __builtin_log2f(l_run);
         }
         return;
     }
     // No merge for these rows: stage them in
-    // LDS ([row][DC] with a 16-byte pad) so that the output stores are whole
+    // LDS ([row][D] with a 16-byte pad) so that the output stores are whole
     // 16-byte pieces of rows.
-    constexpr int RSTR = DC * 2 + 16;                       // staged row stride, bytes
+    constexpr int RSTR = D * 2 + 16;                        // staged row stride, bytes
     static_assert(QROWS * RSTR <= NSTAGE * SLOT, "staging buffer");
     __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));
     __syncthreads();                                        // ring (or merge buffer) free
@@ -558,11 +554,11 @@ attn_bf16_kernel(AttnParams p)
                     u32x2{pack_bf16x2(oacc[dt][i0] * inv, oacc[dt][i0 + 1] * inv),
                           pack_bf16x2(oacc[dt][i0 + 2] * inv, oacc[dt][i0 + 3] * inv)};
             }
-        if (row_ok && half == 0 && dh == 0 && kg == 0 && p.lse)
+        if (row_ok && half == 0 && kg == 0 && p.lse)
             p.lse[((int64_t)b * p.Hq + h) * p.K + qi] = (m_run * c + __builtin_log2f(l_run)) * kLn2;
     }
     __syncthreads();
-    constexpr int PIECES = DC * 2 / 16;                     // 16-byte pieces per row
+    constexpr int PIECES = D * 2 / 16;                      // 16-byte pieces per row
     for (int idx = tid; idx < QROWS * PIECES; idx += 64 * NW) {
         const int row = idx / PIECES;
         const int pc = idx % PIECES;
@@ -571,7 +567,7 @@ attn_bf16_kernel(AttnParams p)
         const u32x4 v = *(const u32x4*)(stage + row * RSTR + pc * 16);
         const int hh_ = g * p.G + rr / p.K;
         uint16_t* dst = (uint16_t*)p.out + (((int64_t)b * p.K + rr % p.K) * p.Hq + hh_) * D;
-        *(u32x4*)(dst + col0 + pc * 8) = v;
+        *(u32x4*)(dst + pc * 8) = v;
     }
 }
 
@@ -871,8 +867,8 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
 // --------------------------------------------------------------------------
 // Deepest K/V ring that fits the 160 KiB of LDS next to the page-id staging
 // (paged) or the query tile (contiguous).
-constexpr int ring_depth(int D, int NR, int DS, bool paged, bool qlds) {
-    const int slot = 64 * D * 2 + 64 * (D / DS) * 2;
+constexpr int ring_depth(int D, int NR, bool paged, bool qlds) {
+    const int slot = 64 * D * 2 * 2;
     const int extra = paged ? kMaxSplitPages * 4 : (qlds ? 32 * NR * D * 2 : 0);
     const int n = (163840 - extra) / slot;
     return n > 6 ? 6 : n;
@@ -881,8 +877,8 @@ constexpr int ring_depth(int D, int NR, int DS, bool paged, bool qlds) {
 // deeper queue delays the first tiles more than it speeds up the last),
 // NSTAGE - 2 when the query tile sits in the last slot (it is read after the
 // first refill could be issued otherwise), within the DMA counter range.
-constexpr int prefetch_depth(int D, int NR, int KS, int DS, int nstage, bool qslot) {
-    const int lpt = (D / 8 + D / DS / 8) / (NR * KS);
+constexpr int prefetch_depth(int D, int NR, int KS, int nstage, bool qslot) {
+    const int lpt = (D / 8 + D / 8) / (NR * KS);
     const int lq = 32 * NR * D * 2 / 1024 / (NR * KS);
     int np = qslot ? nstage - 2 : nstage - 1;
     np = np > 2 ? 2 : np;
@@ -890,18 +886,18 @@ constexpr int prefetch_depth(int D, int NR, int KS, int DS, int nstage, bool qsl
     return np;
 }
 
-template <int D, int NR, int KS, int DS, bool QLDS>
+template <int D, int NR, int KS, bool QLDS>
 static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
-    dim3 grid(p.S_grid * p.B * p.Hkv, p.row_blocks * DS);
+    dim3 grid(p.S_grid * p.B * p.Hkv, p.row_blocks);
     dim3 block(64 * NR * KS);
     if (p.layout == 1) {
-        constexpr int NS = ring_depth(D, NR, DS, true, QLDS);
-        constexpr int NP = prefetch_depth(D, NR, KS, DS, NS, QLDS);
-        hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, DS, NS, NP, true, QLDS>), grid, block, 0, st, p);
+        constexpr int NS = ring_depth(D, NR, true, QLDS);
+        constexpr int NP = prefetch_depth(D, NR, KS, NS, QLDS);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, NS, NP, true, QLDS>), grid, block, 0, st, p);
     } else {
-        constexpr int NS = ring_depth(D, NR, DS, false, QLDS);
-        constexpr int NP = prefetch_depth(D, NR, KS, DS, NS, false);
-        hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, DS, NS, NP, false, QLDS>), grid, block, 0, st, p);
+        constexpr int NS = ring_depth(D, NR, false, QLDS);
+        constexpr int NP = prefetch_depth(D, NR, KS, NS, false);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, NS, NP, false, QLDS>), grid, block, 0, st, p);
     }
     return hipGetLastError();
 }
@@ -927,10 +923,10 @@ static void launch_merge(const AttnParams& p, dim3 grid, hipStream_t st) {
 template <int D>
 static hipError_t launch_bf16_d(const AttnParams& p, hipStream_t st) {
     switch (p.rows_per_wg) {
-        case 32: return launch_bf16<D, 1, 2, 1, true>(p, st);
-        case 64: return launch_bf16<D, 2, 2, 1, true>(p, st);
-        case 128: return launch_bf16<D, 4, 2, 1, true>(p, st);
-        default: return launch_bf16<D, 8, 1, 1, false>(p, st);
+        case 32: return launch_bf16<D, 1, 2, true>(p, st);
+        case 64: return launch_bf16<D, 2, 2, true>(p, st);
+        case 128: return launch_bf16<D, 4, 2, true>(p, st);
+        default: return launch_bf16<D, 8, 1, false>(p, st);
     }
 }
 

@@ -29,7 +29,6 @@ struct AttnParams {
     int layout, mask;
     int SL, S_grid;                   // keys per split (multiple of 64), grid splits
     int rows_per_wg, row_blocks;
-    int ds;                           // output-column split (1 or 2)
     float c;                          // scale * log2(e)
 };
 

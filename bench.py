@@ -184,7 +184,7 @@ class Step:
                           cache_layer_stride=self.kc[0].numel(),
                           blk_layer_stride=self.kb["ar"][0].numel())
 
-    # algorithmic bytes: inputs read once + outputs written once
+    # algorithmic bytes: every input read once, every output written once
     def attn_bytes_per_launch(self):
         c = self.cfg
         e = 2 if c.dtype == "bf16" else 4
@@ -286,8 +286,8 @@ def torch_int(t):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the sharded "
-              "design is described in DESIGN.md, not launched", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); sharding "
+              "over several GPUs is a design, not implemented here", file=sys.stderr)
         sys.exit(2)
     import torch
     import workloads as W

@@ -16,9 +16,14 @@ from ar_shared_kv_amd import api
 from ar_shared_kv_amd import _binding as B_
 
 TOL = {torch.bfloat16: 1e-2, torch.float32: 1e-5}
-# extra guards: relative to the largest |O|, and on lse
+# extra guards, so that a dropped tile cannot hide under the absolute bound:
+# relative to the largest |O|, and on lse.  The bf16 path's row sum is the sum
+# of the bf16-rounded weights (so that O is an exact convex combination of V
+# rows); each carries a relative rounding error of at most 2^-8, so its lse
+# may differ from the exact one by up to -ln(1 - 2^-8) = 3.91e-3 plus fp32
+# terms.  Dropping 1/32 of 2,048 keys moves lse by about 0.03.
 REL_GUARD = {torch.bfloat16: 2e-2, torch.float32: 1e-5}
-LSE_TOL = {torch.bfloat16: 2e-3, torch.float32: 1e-5}
+LSE_TOL = {torch.bfloat16: 4e-3, torch.float32: 1e-5}
 DEV = "cuda"
 
 

@@ -28,6 +28,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
+// Stores of data that the next launch reads.  A relaxed atomic store at agent
+// scope is written through this XCD's L2 (global_store ... sc1), so the data is
+// not left dirty there: the L2 write-back that ends a launch, and that the
+// next launch waits for, then has little to do.
+__device__ __forceinline__ void store_through(void* p, u32x2 v) {
+    __hip_atomic_store((uint64_t*)p, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_through(void* p, f32x4 v) {
+    const u32x4 u = __builtin_bit_cast(u32x4, v);
+    store_through(p, u32x2{u[0], u[1]});
+    store_through((char*)p + 8, u32x2{u[2], u[3]});
+}
+__device__ __forceinline__ void store_through(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Order-preserving map of a float to uint32 (-0.0 and +0.0 map to the same key).
 __device__ __forceinline__ uint32_t float_order_key(float f) {
     uint32_t u = __float_as_uint(f);

@@ -780,30 +780,40 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams p)
 // --------------------------------------------------------------------------
 // Partial blocks [B*Hkv][S_grid][Mpad x D] in fragment order (bf16 on the bf16
 // path, fp32 on the fp32 path), base-2 lse [B*Hkv][S_grid][Mpad].  A work-group
-// of 128 threads covers 32 rows x 16 columns: thread = (row q, 4 columns), so
-// 32 consecutive threads read one contiguous run of a partial block (and of
-// the lse); each thread issues the loads of up to UNROLL splits at once.
-// UNROLL: splits loaded per round (the launch picks about the grid's split
-// count, so that few loads are redundant).
+// covers 32 rows x 16 columns with MG_GROUPS groups of 128 threads: in a group,
+// thread = (row q, 4 columns), so 32 consecutive threads read one contiguous
+// run of a partial block (and of the lse).  Group g merges its own range of
+// about S_grid / MG_GROUPS splits (online log-sum-exp, up to UNROLL loads in
+// flight per thread); the groups' (max, sum, O) are then combined through LDS.
+// Splitting the splits keeps every SIMD busy and the serial weighting chain
+// short (one group over all 32 splits of the Qwen3-8B shape spent 1.5 us in
+// it, after a 2.5 us load round trip).
 // SKIP1: paged launches, whose single-split requests were written by the
 // attention kernel itself.
+constexpr int MG_GROUPS = 4;
+
 template <int D, bool BF16, int UNROLL, bool SKIP1>
-__global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
+__global__ void __launch_bounds__(128 * MG_GROUPS) attn_merge_kernel(AttnParams p)
 {
     const int bh = blockIdx.x;
     const int b = bh / p.Hkv;
     const int g = bh % p.Hkv;
     const int rgrp = blockIdx.y / (D / 16);
     const int cgrp = blockIdx.y % (D / 16);
-    const int q = threadIdx.x & 31;
-    const int quad = threadIdx.x >> 5;                 // 0..3: 4 columns each
+    const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7);   // split group
+    const int tg = threadIdx.x & 127;
+    const int q = tg & 31;
+    const int quad = tg >> 5;                          // 0..3: 4 columns each
     const int r = rgrp * 32 + q;
     const int d = cgrp * 16 + quad * 4;
-    if (r >= p.M) return;
-    const float* lse_r = p.ws_lse + (int64_t)bh * p.S_grid * p.Mpad + r;   // split sp at + sp*Mpad
-    const int64_t blk0 = (int64_t)bh * p.S_grid * p.Mpad * D + frag_offset(r, d, D);
+    const bool row_ok = r < p.M;
+    const int rr = row_ok ? r : 0;                     // rows past M: read row 0, store nothing
+    const float* lse_r = p.ws_lse + (int64_t)bh * p.S_grid * p.Mpad + rr;   // split sp at + sp*Mpad
+    const int64_t blk0 = (int64_t)bh * p.S_grid * p.Mpad * D + frag_offset(rr, d, D);
     const int64_t bstride = (int64_t)p.Mpad * D;
-    auto part = [&](int sp) -> f32x4 {
+    const int spg = (p.S_grid + MG_GROUPS - 1) / MG_GROUPS;    // splits per group
+    const int s_lo = grp * spg;
+    auto part = [&](int sp) __attribute__((always_inline)) -> f32x4 {
         if (BF16) {
             const u32x2 v = *(const u32x2*)((const uint16_t*)p.ws_o + blk0 + sp * bstride);
             return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
@@ -813,8 +823,9 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
     };
     f32x4 v[UNROLL];
     float l2[UNROLL];
-    auto load = [&](int s0) {   // splits s0.. (clamped into the grid; no branches,
-                                // so that all loads are in flight together)
+    auto load = [&](int s0) __attribute__((always_inline)) {
+        // splits s0.. (clamped into the grid; no branches, so that all loads
+        // are in flight together)
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int sp = s0 + u < p.S_grid ? s0 + u : p.S_grid - 1;
@@ -825,19 +836,20 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
     // The first chunk does not depend on lens[b] (splits past S_b are read,
     // then discarded): issue it first so that its round trip and the one of
     // lens overlap.
-    load(0);
+    load(s_lo);
     asm volatile("" ::: "memory");
     const int L = ((const __attribute__((address_space(4))) int32_t*)p.lens)[b];
     int S_b = (L + p.SL - 1) / p.SL;
     S_b = S_b < 1 ? 1 : (S_b > p.S_grid ? p.S_grid : S_b);
-    if (SKIP1 && S_b == 1) return;
+    if (SKIP1 && S_b == 1) return;                     // uniform over the work-group
+    const int s_hi = s_lo + spg < S_b ? s_lo + spg : S_b;
     float mx = -INFINITY;
     float W = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0;;) {
+    for (int s0 = s_lo; s0 < s_hi;) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            if (s0 + u >= S_b) {     // past this request's splits (stale workspace)
+            if (s0 + u >= s_hi) {    // another group's split, or past this request's (stale)
                 l2[u] = -INFINITY;
                 v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
@@ -856,20 +868,43 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p)
         }
         mx = m_new;
         s0 += UNROLL;
-        if (s0 >= S_b) break;
+        if (s0 >= s_hi) break;
         load(s0);
     }
+    // combine the groups (group 0 holds at least split 0, so its max is finite)
+    __shared__ f32x4 s_acc[MG_GROUPS - 1][128];
+    __shared__ f32x2 s_mw[MG_GROUPS - 1][128];
+    if (grp > 0) {
+        s_acc[grp - 1][tg] = acc;
+        s_mw[grp - 1][tg] = f32x2{mx, W};
+    }
+    __syncthreads();
+    if (grp > 0) return;
+    float mt = mx;
+#pragma unroll
+    for (int k = 0; k < MG_GROUPS - 1; ++k) mt = fmaxf(mt, s_mw[k][tg][0]);
+    const float c0 = __builtin_amdgcn_exp2f(mx - mt);
+    W *= c0;
+    acc *= c0;
+#pragma unroll
+    for (int k = 0; k < MG_GROUPS - 1; ++k) {
+        const f32x2 mw = s_mw[k][tg];
+        const float ck = (mw[0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[0] - mt);
+        W += ck * mw[1];
+        acc += ck * s_acc[k][tg];
+    }
+    if (!row_ok) return;
     const float inv = 1.f / W;
     const int hl = r / p.K, qi = r % p.K;
     const int h = g * p.G + hl;
     const int64_t oo = (((int64_t)b * p.K + qi) * p.Hq + h) * D + d;
     if (BF16) {
-        u32x2 v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-        *(u32x2*)((uint16_t*)p.out + oo) = v;
+        u32x2 o = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+        *(u32x2*)((uint16_t*)p.out + oo) = o;
     } else {
         *(f32x4*)((float*)p.out + oo) = acc * inv;
     }
-    if (p.lse && d == 0) p.lse[((int64_t)b * p.Hq + h) * p.K + qi] = (mx + __builtin_log2f(W)) * kLn2;
+    if (p.lse && d == 0) p.lse[((int64_t)b * p.Hq + h) * p.K + qi] = (mt + __builtin_log2f(W)) * kLn2;
 }
 
 // --------------------------------------------------------------------------
@@ -914,14 +949,16 @@ static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
 
 template <int D, bool BF16, bool SKIP1>
 static void launch_merge_u(const AttnParams& p, dim3 grid, hipStream_t st) {
-    if (p.S_grid <= 4)
-        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 4, SKIP1>), grid, dim3(128), 0, st, p);
-    else if (p.S_grid <= 8)
-        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 8, SKIP1>), grid, dim3(128), 0, st, p);
-    else if (p.S_grid <= 16 || !BF16)
-        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 16, SKIP1>), grid, dim3(128), 0, st, p);
+    const int spg = (p.S_grid + MG_GROUPS - 1) / MG_GROUPS;   // splits per group
+    const dim3 block(128 * MG_GROUPS);
+    if (spg <= 2)
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 2, SKIP1>), grid, block, 0, st, p);
+    else if (spg <= 4)
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 4, SKIP1>), grid, block, 0, st, p);
+    else if (spg <= 8)
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 8, SKIP1>), grid, block, 0, st, p);
     else
-        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 32, SKIP1>), grid, dim3(128), 0, st, p);
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 16, SKIP1>), grid, block, 0, st, p);
 }
 
 template <int D, bool BF16>

@@ -16,6 +16,7 @@ constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 constexpr int kTargetWorkGroups = 256;    // one attention work-group per CU on MI355X
 constexpr int kMinKeysPerSplit = 128;     // bf16 (MFMA) path: two tiles per split at least
 constexpr int kMinKeysPerSplitF32 = 64;   // fp32 (vector ALU) path: compute-bound per tile
+constexpr int kLptSplitKeys = 4096;       // paged work-list items (see plan_block_attn)
 constexpr int64_t kMaxGrid = 2147483647;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -71,6 +72,11 @@ AttnPlan plan_block_attn(const orthrus_cache *c, int B, int K, int Hq, int Hkv, 
         const int64_t cap_s =
             ceil_div(lmax, dtype == ORTHRUS_F32 ? kMinKeysPerSplitF32 : kMinKeysPerSplit);
         if (S > cap_s) S = cap_s;
+        // ragged paged batches are scheduled longest-first (the kernel's
+        // work list): items of at most kLptSplitKeys keys pack the CUs evenly
+        if (c->layout == ORTHRUS_LAYOUT_PAGED && dtype == ORTHRUS_BF16 && B <= 64 &&
+            S < ceil_div(lmax, kLptSplitKeys))
+            S = ceil_div(lmax, kLptSplitKeys);
     }
     if (S < 1) S = 1;
     if (c->layout == ORTHRUS_LAYOUT_PAGED && S < ceil_div(lmax, kMaxSplitKeysPaged))
@@ -180,6 +186,8 @@ int orthrus_block_attn(const orthrus_cache *cache, const void *q, const void *k_
     p.rows_per_wg = pl.rows_per_wg;
     p.row_blocks = pl.row_blocks;
     p.c = scale * 1.4426950408889634f;
+    p.lpt = (cache->layout == ORTHRUS_LAYOUT_PAGED && dtype == ORTHRUS_BF16 && B <= 64 &&
+             pl.S_grid > 1) ? 1 : 0;
     if (pl.S_grid > 1) {
         p.ws_o = workspace;
         p.ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.ws_lse_offset);

@@ -56,6 +56,52 @@ __device__ __forceinline__ int64_t frag_offset(int r, int d, int D) {
             + (r & 31)) * 4 + (d & 3);
 }
 
+// Work item of position `pos` in a longest-first list of (request, split)
+// items, for ragged paged batches (B <= 64, one request per lane).  Every
+// request's splits but its last have SL keys; those come first, in (request,
+// split) order, then the last splits by decreasing length (ties by request).
+// The hardware starts work-groups in index order as CUs free up, so this is
+// list scheduling longest-first: the long items no longer start last and
+// leave CUs idle at the end.  Computed by each wave from lens (no DMA is in
+// flight yet, so the vector load does not wait behind one).  Returns false for
+// positions past the last item.
+__device__ __forceinline__ bool lpt_item(const AttnParams& p, int pos, int lane, int& b_out,
+                                         int& s_out) {
+    const bool in = lane < p.B;
+    const int L = in ? p.lens[lane] : 0;
+    int Sb = (L + p.SL - 1) / p.SL;
+    Sb = Sb < 1 ? 1 : (Sb > p.S_grid ? p.S_grid : Sb);
+    const int nfull = in ? Sb - 1 : 0;
+    const int tail = in ? L - (Sb - 1) * p.SL : -1;
+    int incl = nfull;                                  // inclusive scan of nfull
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    const int F = __shfl(incl, 63, 64);                // full splits in the batch
+    const int excl = incl - nfull;
+    if (pos < F) {
+        const uint64_t m = __ballot(in && pos >= excl && pos < incl);
+        const int b = __builtin_ctzll(m);
+        b_out = __builtin_amdgcn_readfirstlane(b);
+        s_out = __builtin_amdgcn_readfirstlane(pos - __shfl(excl, b, 64));
+        return true;
+    }
+    const int want = pos - F;                          // rank among the last splits
+    if (want >= p.B) return false;
+    int rank = 0;
+    for (int j = 0; j < p.B; ++j) {
+        const int tj = __shfl(tail, j, 64);
+        rank += (tj > tail || (tj == tail && j < lane)) ? 1 : 0;
+    }
+    const uint64_t m = __ballot(in && rank == want);
+    const int b = __builtin_ctzll(m);
+    b_out = __builtin_amdgcn_readfirstlane(b);
+    s_out = __builtin_amdgcn_readfirstlane(__shfl(Sb, b, 64) - 1);
+    return true;
+}
+
 // --------------------------------------------------------------------------
 // bf16 MFMA kernel
 // --------------------------------------------------------------------------
@@ -110,8 +156,14 @@ attn_bf16_kernel(AttnParams p)
     const int rg = wave % NR;      // row group
     const int kg = wave / NR;      // key slice
     const int BH = p.B * p.Hkv;
-    const int bh = blockIdx.x % BH;
-    const int s = blockIdx.x / BH;
+    int bh = blockIdx.x % BH;
+    int s = blockIdx.x / BH;
+    if (PAGED && p.lpt) {             // longest-first work list
+        int bi, si;
+        if (!lpt_item(p, blockIdx.x / p.Hkv, lane, bi, si)) return;
+        bh = bi * p.Hkv + blockIdx.x % p.Hkv;
+        s = si;
+    }
     const int b = bh / p.Hkv;
     const int g = bh % p.Hkv;
     const int rb = blockIdx.y;        // row block
@@ -780,20 +832,21 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams p)
 // --------------------------------------------------------------------------
 // Partial blocks [B*Hkv][S_grid][Mpad x D] in fragment order (bf16 on the bf16
 // path, fp32 on the fp32 path), base-2 lse [B*Hkv][S_grid][Mpad].  A work-group
-// covers 32 rows x 16 columns with MG_GROUPS groups of 128 threads: in a group,
+// covers 32 rows x 16 columns with NG groups of 128 threads: in a group,
 // thread = (row q, 4 columns), so 32 consecutive threads read one contiguous
 // run of a partial block (and of the lse).  Group g merges its own range of
-// about S_grid / MG_GROUPS splits (online log-sum-exp, up to UNROLL loads in
-// flight per thread); the groups' (max, sum, O) are then combined through LDS.
+// about S_grid / NG splits (online log-sum-exp, up to UNROLL loads in flight
+// per thread); the groups' (max, sum, O) are then combined through LDS.
 // Splitting the splits keeps every SIMD busy and the serial weighting chain
-// short (one group over all 32 splits of the Qwen3-8B shape spent 1.5 us in
-// it, after a 2.5 us load round trip).
+// short when there are many (one group over all 32 splits of the Qwen3-8B
+// shape spent 1.5 us in it, after a 2.5 us load round trip); with a few
+// splits one group does it, and the grid's many small work-groups start
+// sooner (NG = 4 over 3 splits took 18 us instead of 6 on a 32-request paged
+// batch).
 // SKIP1: paged launches, whose single-split requests were written by the
 // attention kernel itself.
-constexpr int MG_GROUPS = 4;
-
-template <int D, bool BF16, int UNROLL, bool SKIP1>
-__global__ void __launch_bounds__(128 * MG_GROUPS) attn_merge_kernel(AttnParams p)
+template <int D, bool BF16, int UNROLL, bool SKIP1, int NG>
+__global__ void __launch_bounds__(128 * NG) attn_merge_kernel(AttnParams p)
 {
     const int bh = blockIdx.x;
     const int b = bh / p.Hkv;
@@ -811,7 +864,7 @@ __global__ void __launch_bounds__(128 * MG_GROUPS) attn_merge_kernel(AttnParams 
     const float* lse_r = p.ws_lse + (int64_t)bh * p.S_grid * p.Mpad + rr;   // split sp at + sp*Mpad
     const int64_t blk0 = (int64_t)bh * p.S_grid * p.Mpad * D + frag_offset(rr, d, D);
     const int64_t bstride = (int64_t)p.Mpad * D;
-    const int spg = (p.S_grid + MG_GROUPS - 1) / MG_GROUPS;    // splits per group
+    const int spg = (p.S_grid + NG - 1) / NG;    // splits per group
     const int s_lo = grp * spg;
     auto part = [&](int sp) __attribute__((always_inline)) -> f32x4 {
         if (BF16) {
@@ -872,26 +925,28 @@ __global__ void __launch_bounds__(128 * MG_GROUPS) attn_merge_kernel(AttnParams 
         load(s0);
     }
     // combine the groups (group 0 holds at least split 0, so its max is finite)
-    __shared__ f32x4 s_acc[MG_GROUPS - 1][128];
-    __shared__ f32x2 s_mw[MG_GROUPS - 1][128];
-    if (grp > 0) {
-        s_acc[grp - 1][tg] = acc;
-        s_mw[grp - 1][tg] = f32x2{mx, W};
-    }
-    __syncthreads();
-    if (grp > 0) return;
     float mt = mx;
+    if constexpr (NG > 1) {
+        __shared__ f32x4 s_acc[NG - 1][128];
+        __shared__ f32x2 s_mw[NG - 1][128];
+        if (grp > 0) {
+            s_acc[grp - 1][tg] = acc;
+            s_mw[grp - 1][tg] = f32x2{mx, W};
+        }
+        __syncthreads();
+        if (grp > 0) return;
 #pragma unroll
-    for (int k = 0; k < MG_GROUPS - 1; ++k) mt = fmaxf(mt, s_mw[k][tg][0]);
-    const float c0 = __builtin_amdgcn_exp2f(mx - mt);
-    W *= c0;
-    acc *= c0;
+        for (int k = 0; k < NG - 1; ++k) mt = fmaxf(mt, s_mw[k][tg][0]);
+        const float c0 = __builtin_amdgcn_exp2f(mx - mt);
+        W *= c0;
+        acc *= c0;
 #pragma unroll
-    for (int k = 0; k < MG_GROUPS - 1; ++k) {
-        const f32x2 mw = s_mw[k][tg];
-        const float ck = (mw[0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[0] - mt);
-        W += ck * mw[1];
-        acc += ck * s_acc[k][tg];
+        for (int k = 0; k < NG - 1; ++k) {
+            const f32x2 mw = s_mw[k][tg];
+            const float ck = (mw[0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[0] - mt);
+            W += ck * mw[1];
+            acc += ck * s_acc[k][tg];
+        }
     }
     if (!row_ok) return;
     const float inv = 1.f / W;
@@ -949,16 +1004,16 @@ static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
 
 template <int D, bool BF16, bool SKIP1>
 static void launch_merge_u(const AttnParams& p, dim3 grid, hipStream_t st) {
-    const int spg = (p.S_grid + MG_GROUPS - 1) / MG_GROUPS;   // splits per group
-    const dim3 block(128 * MG_GROUPS);
-    if (spg <= 2)
-        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 2, SKIP1>), grid, block, 0, st, p);
-    else if (spg <= 4)
-        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 4, SKIP1>), grid, block, 0, st, p);
-    else if (spg <= 8)
-        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 8, SKIP1>), grid, block, 0, st, p);
+    if (p.S_grid <= 2)
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 2, SKIP1, 1>), grid, dim3(128), 0, st, p);
+    else if (p.S_grid <= 4)
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 4, SKIP1, 1>), grid, dim3(128), 0, st, p);
+    else if (p.S_grid <= 16)   // four groups of up to 4 splits
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 4, SKIP1, 4>), grid, dim3(512), 0, st, p);
+    else if (p.S_grid <= 32)
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 8, SKIP1, 4>), grid, dim3(512), 0, st, p);
     else
-        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 16, SKIP1>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((attn_merge_kernel<D, BF16, 16, SKIP1, 4>), grid, dim3(512), 0, st, p);
 }
 
 template <int D, bool BF16>

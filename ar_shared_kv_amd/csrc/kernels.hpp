@@ -30,6 +30,8 @@ struct AttnParams {
     int SL, S_grid;                   // keys per split (multiple of 64), grid splits
     int rows_per_wg, row_blocks;
     float c;                          // scale * log2(e)
+    int lpt;                          // paged, B <= 64: blockIdx.x walks a longest-first
+                                      // list of (request, split) work items
 };
 
 int attn_rows_per_wg(int dtype, int M);

@@ -110,8 +110,10 @@ __device__ __forceinline__ bool lpt_item(const AttnParams& p, int pos, int lane,
 // slots; NPRE: tiles kept in
 // flight ahead of the one being computed; QLDS: the query tile is fetched by
 // LDS DMA as part of the prologue instead of through VGPR loads.
+// Two work-groups per CU (a 2-slot ring) keep 64-row work-groups within 256
+// registers per lane.
 template <int D, int NR, int KS, int NSTAGE, int NPRE, bool PAGED, bool QLDS>
-__global__ void __launch_bounds__(64 * NR * KS)
+__global__ void __launch_bounds__(64 * NR * KS, (NR == 2 && NSTAGE == 2) ? 2 : 1)
 attn_bf16_kernel(AttnParams p)
 {
     constexpr int NW = NR * KS;
@@ -994,6 +996,17 @@ static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
         constexpr int NS = ring_depth(D, NR, true, QLDS);
         constexpr int NP = prefetch_depth(D, NR, KS, NS, QLDS);
         hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, NS, NP, true, QLDS>), grid, block, 0, st, p);
+    } else if (NR <= 2 && (NR == 2 || (int64_t)grid.x * grid.y > 256)) {
+        // Contiguous 64-row work-groups, and 32-row ones when the grid has
+        // more work-groups than CUs: a 2-slot ring, one tile in flight while
+        // another is computed, so that two work-groups share a CU and one's
+        // start-up and drain overlap the other's streaming (131,072 keys,
+        // 64 splits, K = 4 / 8 / 16: 111 -> 98, 116 -> 97, 111 -> 99 us per
+        // layer pass; 8,192 keys, K = 16: 15.5 -> 14.8 us).  With at most
+        // one 32-row work-group per CU the deep ring is faster (32,768 keys,
+        // K = 8: 32.0 vs 36.2 us).
+        if constexpr (NR <= 2)
+            hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, 2, 1, false, QLDS>), grid, block, 0, st, p);
     } else {
         constexpr int NS = ring_depth(D, NR, false, QLDS);
         constexpr int NP = prefetch_depth(D, NR, KS, NS, false);

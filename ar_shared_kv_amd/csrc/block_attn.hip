@@ -418,14 +418,10 @@ attn_bf16_kernel(AttnParams p)
     // before that tile (the last one; they still pass its arrival barrier),
     // which leaves the SIMD to the other slice on the last split's critical
     // path.
-    const int n_loop = n_tiles - ((KS > 1 && last && kg * KPW >= p.K) ? 1 : 0);
-    for (int t = 0; t < n_loop; ++t) {
-
-        const uint16_t* Vs = (const uint16_t*)(smem + (t % NSTAGE) * SLOT + K_BYTES);
-        const bool is_blk = t >= n_cache_tiles;
-        const int start = is_blk ? 0 : kbeg + t * TK;
-        const int count = is_blk ? p.K : (kend - start < TK ? kend - start : TK);
-
+    // One tile: mask, online softmax, P V.  Force-inlined, so that the steady
+    // loop below gets it with the full-tile arguments folded in.
+    auto tile = [&](int t, const uint16_t* Vs, bool is_blk, int count)
+        __attribute__((always_inline)) {
         // ---- mask (partial cache tile, or the block tile) ----
         const bool need_mask = is_blk ? (p.mask == 1 || count < TK) : (count < TK);
         if (need_mask) {
@@ -508,6 +504,33 @@ attn_bf16_kernel(AttnParams p)
                     oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8, vf[dt]), pb[kb][hh], oacc[dt], 0, 0, 0);
             }
+    };
+
+    const int n_loop = n_tiles - ((KS > 1 && last && kg * KPW >= p.K) ? 1 : 0);
+    // Steady state first: full cache tiles whose refill is a full cache tile
+    // too.  Every test of the general loop below (partial or block tile, mask,
+    // tiles left to issue, how many may still fly) is then known, and its
+    // scalar branches leave the per-tile instruction stream.
+    const int n_full = (kend - kbeg) / TK;
+    const int n_fast = n_full - 1 - NPRE > 0 ? n_full - 1 - NPRE : 0;
+    int t = 0;
+    for (; t < n_fast; ++t) {
+        tile(t, (const uint16_t*)(smem + (t % NSTAGE) * SLOT + K_BYTES), false, TK);
+        // arrive(t + 1): NPRE - 1 later tiles may fly; refill tile t + 1 + NPRE
+        __builtin_amdgcn_s_waitcnt(vmcnt_encode((NPRE - 1) * LPT));
+        __syncthreads();
+        issue_rows(t + 1 + NPRE, false, kbeg + (t + 1 + NPRE) * TK, TK);
+        last_issued = t + 1 + NPRE;
+        qk(t + 1, scur);
+    }
+    for (; t < n_loop; ++t) {
+
+        const uint16_t* Vs = (const uint16_t*)(smem + (t % NSTAGE) * SLOT + K_BYTES);
+        const bool is_blk = t >= n_cache_tiles;
+        const int start = is_blk ? 0 : kbeg + t * TK;
+        const int count = is_blk ? p.K : (kend - start < TK ? kend - start : TK);
+
+        tile(t, Vs, is_blk, count);
         // Only now wait for the next tile: everything this tile allows is
         // issued, so after the last tile lands only its own work remains.  Its
         // scores go to the matrix cores behind this tile's P V.

@@ -20,12 +20,16 @@
 //    in-lane plus one permlane32 swap; exp2 with log2(e) folded into the
 //    scale; row sums of the bf16-rounded weights on the matrix cores.
 //  * Split-KV: each split writes its normalised partial O (in the path's
-//    dtype, in MFMA fragment order) and its base-2 log-sum-exp; a second
-//    launch merges them (attn_merge_kernel).  The block rows are processed by
-//    the last split of each request.
+//    dtype, in MFMA fragment order) and its base-2 log-sum-exp through the
+//    L2; a second launch merges them (attn_merge_kernel).  The block rows are
+//    processed by the last split of each request.
 //  * blockIdx.x = split * (B*Hkv) + (b*Hkv + g): with B*Hkv a multiple of 8
 //    every split of one KV head lands on the same XCD (work-groups are dealt
 //    round-robin over the 8 XCDs), sharing that XCD's L2 for the query tile.
+//    Ragged paged batches instead walk a longest-first list of (request,
+//    split) items.
+//  * Full tiles run in a steady loop with every per-tile test resolved; small
+//    work-groups (32 or 64 rows) take a 2-slot ring so that two share a CU.
 #include "common.hpp"
 #include "kernels.hpp"
 

@@ -124,10 +124,10 @@ __device__ __forceinline__ bool lpt_item(const AttnParams& p, int pos, int lane,
 // slots; NPRE: tiles kept in
 // flight ahead of the one being computed; QLDS: the query tile is fetched by
 // LDS DMA as part of the prologue instead of through VGPR loads.
-// Two work-groups per CU (a 2-slot ring) keep 64-row work-groups within 256
-// registers per lane.
+// Two work-groups per CU (a 2-slot ring) keep four-wave work-groups (64 rows
+// in two key slices, or 128 rows in one) within 256 registers per lane.
 template <int D, int NR, int KS, int NSTAGE, int NPRE, bool PAGED, bool QLDS>
-__global__ void __launch_bounds__(64 * NR * KS, (NR == 2 && NSTAGE == 2) ? 2 : 1)
+__global__ void __launch_bounds__(64 * NR * KS, (NR * KS == 4 && NSTAGE == 2) ? 2 : 1)
 attn_bf16_kernel(AttnParams p)
 {
     constexpr int NW = NR * KS;
@@ -1041,7 +1041,7 @@ static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
         constexpr int NS = ring_depth(D, NR, true, QLDS);
         constexpr int NP = prefetch_depth(D, NR, KS, NS, QLDS);
         hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, NS, NP, true, QLDS>), grid, block, 0, st, p);
-    } else if (NR <= 2 && (NR == 2 || (int64_t)grid.x * grid.y > 256)) {
+    } else if ((NR <= 2 && (NR == 2 || (int64_t)grid.x * grid.y > 256)) || (NR == 4 && KS == 1)) {
         // Contiguous 64-row work-groups, and 32-row ones when the grid has
         // more work-groups than CUs: a 2-slot ring, one tile in flight while
         // another is computed, so that two work-groups share a CU and one's
@@ -1049,8 +1049,9 @@ static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
         // 64 splits, K = 4 / 8 / 16: 111 -> 98, 116 -> 97, 111 -> 99 us per
         // layer pass; 8,192 keys, K = 16: 15.5 -> 14.8 us).  With at most
         // one 32-row work-group per CU the deep ring is faster (32,768 keys,
-        // K = 8: 32.0 vs 36.2 us).
-        if constexpr (NR <= 2)
+        // K = 8: 32.0 vs 36.2 us).  128-row work-groups come here as four
+        // waves (KS = 1) when they outnumber the CUs.
+        if constexpr (NR <= 2 || (NR == 4 && KS == 1))
             hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, 2, 1, false, QLDS>), grid, block, 0, st, p);
     } else {
         constexpr int NS = ring_depth(D, NR, false, QLDS);
@@ -1085,7 +1086,14 @@ static hipError_t launch_bf16_d(const AttnParams& p, hipStream_t st) {
     switch (p.rows_per_wg) {
         case 32: return launch_bf16<D, 1, 2, true>(p, st);
         case 64: return launch_bf16<D, 2, 2, true>(p, st);
-        case 128: return launch_bf16<D, 4, 2, true>(p, st);
+        case 128:
+            // more contiguous work-groups than CUs: four waves each, so that
+            // two share a CU (131,072 keys, K = 32, 64 splits: 263 -> 250 us
+            // per step, 58 -> 60.5% of HBM peak); the query then lives in
+            // VGPRs to leave the LDS to two 2-slot rings
+            if (p.layout == 0 && (int64_t)p.S_grid * p.B * p.Hkv * p.row_blocks > 256)
+                return launch_bf16<D, 4, 1, false>(p, st);
+            return launch_bf16<D, 4, 2, true>(p, st);
         default: return launch_bf16<D, 8, 1, false>(p, st);
     }
 }

@@ -111,6 +111,9 @@ EDGE = [
     ("M48", 2, 12, 4, 128, 16, [1500, 40], "bf16", False),
     # 320 work-groups of 8 rows: more than the CUs, so two share a CU (2-slot ring)
     ("M8-two-per-CU", 40, 8, 8, 128, 8, [(97 * i) % 700 for i in range(40)], "bf16", False),
+    # 288 work-groups of 128 rows (3 splits each): two share a CU, four waves
+    # each taking whole 64-key tiles
+    ("M128-two-per-CU", 12, 32, 8, 128, 32, [(211 * i) % 1500 for i in range(12)], "bf16", False),
     ("paged-ragged", 4, 8, 2, 128, 9, [0, 17, 300, 1100], "bf16", True),
     ("paged-D64", 2, 4, 1, 64, 32, [16, 47], "bf16", True),
     ("fp32-ragged", 2, 4, 2, 128, 5, [70, 3], "f32", False),

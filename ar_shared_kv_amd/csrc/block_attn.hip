@@ -28,8 +28,10 @@
 //    round-robin over the 8 XCDs), sharing that XCD's L2 for the query tile.
 //    Ragged paged batches instead walk a longest-first list of (request,
 //    split) items.
-//  * Full tiles run in a steady loop with every per-tile test resolved; small
-//    work-groups (32 or 64 rows) take a 2-slot ring so that two share a CU.
+//  * Full tiles run in a steady loop with every per-tile test resolved;
+//    work-groups of at most four waves (32 or 64 rows, or 128 rows in one key
+//    slice when they outnumber the CUs) take a 2-slot ring so that two share
+//    a CU.
 #include "common.hpp"
 #include "kernels.hpp"
 

@@ -21,7 +21,11 @@ constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 constexpr int kTargetWorkGroups = 208;
 constexpr int kMinKeysPerSplit = 128;     // bf16 (MFMA) path: two tiles per split at least
 constexpr int kMinKeysPerSplitF32 = 64;   // fp32 (vector ALU) path: compute-bound per tile
-constexpr int kLptSplitKeys = 4096;       // paged work-list items (see plan_block_attn)
+// Paged work-list items (see plan_block_attn).  32 requests of 512..8,192
+// keys, A/B on one box: 2,560-key items 176 us per layer pass, 3,072: 152,
+// 3,584: 152, 4,096: 164 (items per CU decide: about two, paired long with
+// short, pack best).
+constexpr int kLptSplitKeys = 3584;
 constexpr int64_t kMaxGrid = 2147483647;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -115,6 +115,10 @@ EDGE = [
     # each taking whole 64-key tiles
     ("M128-two-per-CU", 12, 32, 8, 128, 32, [(211 * i) % 1500 for i in range(12)], "bf16", False),
     ("paged-ragged", 4, 8, 2, 128, 9, [0, 17, 300, 1100], "bf16", True),
+    # the longest-first work list decodes one request per lane: 64 requests is
+    # its limit (equal tails test the rank's tie-break); 65 takes the plain grid
+    ("paged-B64-worklist", 64, 8, 2, 128, 8, [100 * ((7 * i) % 9) for i in range(64)], "bf16", True),
+    ("paged-B65-plain", 65, 8, 2, 128, 8, [100 * ((7 * i) % 9) for i in range(65)], "bf16", True),
     ("paged-D64", 2, 4, 1, 64, 32, [16, 47], "bf16", True),
     ("fp32-ragged", 2, 4, 2, 128, 5, [70, 3], "f32", False),
     ("fp32-paged", 2, 2, 1, 64, 8, [130, 0], "f32", True),

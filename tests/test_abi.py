@@ -95,6 +95,34 @@ def test_block_attn_workspace_formula():
     assert B.orthrus_block_attn_workspace_bytes(c, 1, 64, 32, 8, 96, B.BF16, 0) == 0   # invalid
 
 
+def _splits(c, B_, K, Hq, Hkv, D=128, dtype=B.BF16, num_splits=0):
+    """Split count of the automatic plan, read back from the workspace size."""
+    n = B.orthrus_block_attn_workspace_bytes(c, B_, K, Hq, Hkv, D, dtype, num_splits)
+    if n == 0:
+        return 1
+    mpad = -(-(Hq // Hkv) * K // 32) * 32
+    per_split = B_ * Hkv * mpad
+    for s in range(1, 4097):
+        if -(-per_split * s * D * 2 // 256) * 256 + per_split * s * 4 == n:
+            return s
+    raise AssertionError(f"no split count gives {n} bytes")
+
+
+def test_automatic_split_plan_of_the_workloads():
+    # Qwen3-8B shape, L = 8,192, K = 32: 26 splits of 320 keys -> 208 work-groups
+    assert _splits(cache(capacity=8224, max_len=8192), 1, 32, 32, 8) == 26
+    # Qwen3-1.7B layer, L = 2,048: the 128-key minimum decides (16 splits)
+    assert _splits(cache(capacity=2080, max_len=2048), 1, 32, 16, 8) == 16
+    # 131,072 keys with the workload's explicit 64 partitions
+    assert _splits(cache(capacity=131136, max_len=131072), 1, 32, 32, 8, num_splits=64) == 64
+    # paged, 32 requests up to 8,192 keys (+32 appended rows): work-list items of
+    # at most 3,584 keys -> 3 split slots per request over the page table's range
+    pc = cache(layout=B.PAGED, pages=20000, maxp=515, max_len=0)
+    assert _splits(pc, 32, 32, 32, 8) == 3
+    # no split below two tiles of keys
+    assert _splits(cache(capacity=200, max_len=128), 1, 32, 32, 8) == 1
+
+
 def test_consensus_validation_and_workspace():
     f = B.lib().orthrus_consensus
     args = [FAKE, FAKE, 1, 32, 151936, B.BF16] + [FAKE] * 7

@@ -120,6 +120,10 @@ EDGE = [
     ("paged-B64-worklist", 64, 8, 2, 128, 8, [100 * ((7 * i) % 9) for i in range(64)], "bf16", True),
     ("paged-B65-plain", 65, 8, 2, 128, 8, [100 * ((7 * i) % 9) for i in range(65)], "bf16", True),
     ("paged-D64", 2, 4, 1, 64, 32, [16, 47], "bf16", True),
+    # D = 64 through the work list with several splits per request, and K = 1
+    # (one query row per head) on pages
+    ("paged-D64-worklist", 24, 8, 2, 64, 16, [(409 * i) % 3000 for i in range(24)], "bf16", True),
+    ("paged-K1", 5, 8, 8, 128, 1, [1, 700, 64, 0, 2049], "bf16", True),
     ("fp32-ragged", 2, 4, 2, 128, 5, [70, 3], "f32", False),
     ("fp32-paged", 2, 2, 1, 64, 8, [130, 0], "f32", True),
 ]

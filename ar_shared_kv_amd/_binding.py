@@ -61,6 +61,8 @@ SIGNATURES = {
     "orthrus_consensus_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "orthrus_argmax": (_I, [_P, _I64, _I, _I, _P, _P, _SZ, _P]),
     "orthrus_argmax_workspace_bytes": (_SZ, [_I64, _I, _I]),
+    "orthrus_lmhead_argmax": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "orthrus_lmhead_argmax_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "orthrus_kv_append": (_I, [_CP, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I64, _P]),
     "orthrus_status_string": (ctypes.c_char_p, [_I]),
     "orthrus_version": (_I, []),
@@ -175,6 +177,17 @@ def orthrus_argmax(logits, rows, V, dtype, idx, workspace, workspace_bytes, stre
 
 def orthrus_argmax_workspace_bytes(rows, V, dtype) -> int:
     return lib().orthrus_argmax_workspace_bytes(rows, V, dtype)
+
+
+def orthrus_lmhead_argmax(hidden, weight, R, H, V, dtype, idx, workspace, workspace_bytes,
+                          stream=None) -> int:
+    return lib().orthrus_lmhead_argmax(ptr(hidden), ptr(weight), R, H, V, dtype, ptr(idx),
+                                       ptr(workspace), workspace_bytes,
+                                       stream if isinstance(stream, int) else stream_handle(stream))
+
+
+def orthrus_lmhead_argmax_workspace_bytes(R, H, V, dtype) -> int:
+    return lib().orthrus_lmhead_argmax_workspace_bytes(R, H, V, dtype)
 
 
 def orthrus_kv_append(cache, k_blk, v_blk, n_emit, lens_out, B, K, Hkv, D, dtype, num_layers,

@@ -96,6 +96,23 @@ def argmax(logits, stream=None):
     return idx.view(logits.shape[:-1])
 
 
+def lmhead_argmax(hidden, weight, idx=None, workspace=None, stream=None):
+    """Greedy tokens of hidden [..., H] under the LM head weight [V, H] (bf16)."""
+    H = hidden.shape[-1]
+    R = hidden.numel() // H
+    V = weight.shape[0]
+    dt = dtype_code(hidden)
+    if idx is None:
+        idx = torch.empty(R, dtype=torch.int32, device=hidden.device)
+    n = B_.orthrus_lmhead_argmax_workspace_bytes(R, H, V, dt)
+    if workspace is None:
+        workspace = torch.empty(max(n, 8), dtype=torch.uint8, device=hidden.device)
+    st = B_.orthrus_lmhead_argmax(hidden, weight, R, H, V, dt, idx, workspace,
+                                  workspace.numel(), stream)
+    B_.check("orthrus_lmhead_argmax", st)
+    return idx.view(hidden.shape[:-1])
+
+
 def kv_append(cache, k_blk, v_blk, n_emit, lens_out=None, *, num_layers=1,
               cache_layer_stride=0, blk_layer_stride=0, stream=None):
     """Append accepted AR rows; k_blk/v_blk are layer 0's [B, K, Hkv, D]."""

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OUT = os.path.join(HERE, "liborthrus.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["abi.cpp", "block_attn.hip", "consensus.hip", "kv_append.hip"]
+SOURCES = ["abi.cpp", "block_attn.hip", "consensus.hip", "kv_append.hip", "lmhead.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

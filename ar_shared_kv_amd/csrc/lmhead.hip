@@ -1,0 +1,179 @@
+// Greedy prediction straight from the hidden states: the LM head's logits
+// row . W^T and their row argmax in one pass, without writing the logits.
+//
+// Operation (Orthrus summary on gist.science, §2.3: both views predict
+// greedily from their final hidden states; the consensus compares the two
+// argmax tokens): idx[r] = argmax_v sum_k x[r][k] * w[v][k], lowest index on
+// ties, for R rows of H hidden values and a V x H weight matrix.
+//
+// Design (MI355X): decode has few rows (R = B*K, 32 at the Qwen3-8B shape)
+// against V = 151,936 vocabulary rows, so the weight matrix is read once and
+// the work is HBM-bound.  One work-group per (128 vocabulary rows, 32 hidden
+// rows): 128 x 128 weight chunks and the matching 32 x 128 hidden chunk
+// stream HBM -> LDS with global_load_lds (16-byte granules XOR-swizzled per
+// row), two chunks in flight per CU (two work-groups of a 2-slot ring each).
+// Each wave owns 32 vocabulary rows: logits^T = W x^T on the matrix cores
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation over H), then a (value,
+// lowest index) key per hidden row is reduced over the lanes, the waves and,
+// in a second launch, over the vocabulary blocks.
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include "../../include/orthrus.h"
+
+namespace orthrus {
+
+namespace {
+
+constexpr int kLmVB = 128;                    // vocabulary rows per work-group
+constexpr int kLmHC = 128;                    // hidden columns per chunk
+constexpr int kLmRB = 32;                     // hidden rows per work-group
+constexpr int kLmWBytes = kLmVB * kLmHC * 2;  // 32 KiB of weights per chunk
+constexpr int kLmXBytes = kLmRB * kLmHC * 2;  // 8 KiB of hidden states per chunk
+constexpr int kLmSlot = kLmWBytes + kLmXBytes;
+constexpr int kLmStages = 2;
+constexpr int kLmLoads = (kLmWBytes + kLmXBytes) / (256 * 16);   // DMA loads per lane per chunk
+
+// 16-byte global -> LDS copy per lane (lane l lands at lds + 16*l); the waits
+// are the explicit s_waitcnt of the chunk loop.
+__device__ __forceinline__ void lm_dma16(const void* gptr, uint32_t lds_addr) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(m0)
+                 : "memory", "m0");
+}
+
+__global__ void __launch_bounds__(256, 2)
+lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int R, int H,
+                     int V, int nvb, uint64_t* __restrict__ ws)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[kLmStages * kLmSlot];
+    __shared__ uint64_t red[4][32];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int half = lane >> 5;
+    const int vb = blockIdx.x;
+    const int v0 = vb * kLmVB;
+    const int r0 = blockIdx.y * kLmRB;
+    const int nchunk = H / kLmHC;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(ORTHRUS_LDS void*)&smem[0];
+
+    // DMA of chunk c into slot c % 2.  A 1 KiB wave load covers 4 rows of
+    // 16 granules; lane l writes LDS granule l % 16 of row 4k + l / 16 with the
+    // global granule (l % 16) ^ (row % 16), so that granule g of a row sits at
+    // g ^ (row % 16) and the fragment reads below hit distinct banks.
+    auto issue = [&](int c) __attribute__((always_inline)) {
+        const uint32_t slot = lds_base + (uint32_t)((c % kLmStages) * kLmSlot);
+        const int col = c * kLmHC;
+#pragma unroll
+        for (int i = 0; i < kLmLoads; ++i) {
+            const int k = i * 4 + wave;                  // 1 KiB piece of the slot
+            const bool isx = k >= kLmWBytes / 1024;
+            const int row = (isx ? k - kLmWBytes / 1024 : k) * 4 + lane / 16;
+            const int gsrc = (lane % 16) ^ (row % 16);
+            const uint16_t* src;
+            if (isx) {
+                const int rr = r0 + row < R ? r0 + row : R - 1;
+                src = x + (int64_t)rr * H + col + gsrc * 8;
+            } else {
+                const int vv = v0 + row < V ? v0 + row : V - 1;
+                src = w + (int64_t)vv * H + col + gsrc * 8;
+            }
+            lm_dma16(src, slot + (uint32_t)(k * 1024));
+        }
+    };
+
+    f32x16 acc = f32x16{};
+    const int vrow = wave * 32 + (lane & 31);            // this lane's vocabulary row (A operand)
+    const int xrow = lane & 31;                          // this lane's hidden row (B operand)
+    issue(0);
+    for (int c = 0; c < nchunk; ++c) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));     // chunk c landed (this lane's part)
+        __syncthreads();                                 // ... everyone's; slot (c+1)%2 is free
+        if (c + 1 < nchunk) issue(c + 1);
+        const char* Ws = smem + (c % kLmStages) * kLmSlot;
+        const char* Xs = Ws + kLmWBytes;
+        u32x4 af[kLmHC / 16], bfr[kLmHC / 16];
+#pragma unroll
+        for (int ds = 0; ds < kLmHC / 16; ++ds) {
+            const int g = 2 * ds + half;
+            af[ds] = *(const u32x4*)(Ws + vrow * (kLmHC * 2) + ((g ^ (vrow % 16)) * 16));
+            bfr[ds] = *(const u32x4*)(Xs + xrow * (kLmHC * 2) + ((g ^ (xrow % 16)) * 16));
+        }
+#pragma unroll
+        for (int ds = 0; ds < kLmHC / 16; ++ds)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[ds]),
+                                                          __builtin_bit_cast(bf16x8, bfr[ds]),
+                                                          acc, 0, 0, 0);
+    }
+
+    // acc[i] = logit of vocabulary row v0 + 32*wave + 8*(i/4) + 4*half + i%4
+    // for hidden row r0 + lane%32
+    uint64_t key = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int v = v0 + wave * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (v < V) {
+            const uint64_t k = argmax_key(acc[i], (uint32_t)v);
+            key = k > key ? k : key;
+        }
+    }
+    const uint64_t o = shfl_xor_u64(key, 32);
+    key = o > key ? o : key;
+    if (lane < 32) red[wave][lane] = key;
+    __syncthreads();
+    if (tid < 32) {
+        uint64_t k = red[0][tid];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) k = red[q][tid] > k ? red[q][tid] : k;
+        if (r0 + tid < R) ws[(int64_t)(r0 + tid) * nvb + vb] = k;
+    }
+}
+
+int64_t lm_blocks(int V) { return ((int64_t)V + kLmVB - 1) / kLmVB; }
+
+bool lm_shape_ok(int R, int H, int V) {
+    return R >= 1 && R <= 65535 * kLmRB && H >= kLmHC && H % kLmHC == 0 && H <= 65536 && V >= 1;
+}
+
+}  // namespace
+
+}  // namespace orthrus
+
+using namespace orthrus;
+
+extern "C" {
+
+size_t orthrus_lmhead_argmax_workspace_bytes(int R, int H, int V, int dtype)
+{
+    if (dtype != ORTHRUS_BF16 || !lm_shape_ok(R, H, V)) return 0;
+    return (size_t)R * (size_t)lm_blocks(V) * sizeof(uint64_t);
+}
+
+int orthrus_lmhead_argmax(const void *hidden, const void *weight, int R, int H, int V, int dtype,
+                          int32_t *idx, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream)
+{
+    if (!hidden || !weight || !idx) return ORTHRUS_ERR_NULL;
+    if (dtype != ORTHRUS_BF16 && dtype != ORTHRUS_F32) return ORTHRUS_ERR_DTYPE;
+    if (R < 1 || H < 1 || V < 1) return ORTHRUS_ERR_SHAPE;
+    if (dtype != ORTHRUS_BF16 || !lm_shape_ok(R, H, V)) return ORTHRUS_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(hidden) & 15u) || (reinterpret_cast<uintptr_t>(weight) & 15u))
+        return ORTHRUS_ERR_UNSUPPORTED;
+    const int64_t nvb = lm_blocks(V);
+    const size_t need = (size_t)R * (size_t)nvb * sizeof(uint64_t);
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 7u))
+        return ORTHRUS_ERR_WORKSPACE;
+    uint64_t *ws = static_cast<uint64_t *>(workspace);
+    const dim3 grid((unsigned)nvb, (unsigned)((R + kLmRB - 1) / kLmRB));
+    hipLaunchKernelGGL(lmhead_argmax_kernel, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(hidden), static_cast<const uint16_t *>(weight),
+                       R, H, V, (int)nvb, ws);
+    if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
+    return launch_argmax_finalize(ws, R, (int)nvb, idx, stream) == hipSuccess ? ORTHRUS_OK
+                                                                               : ORTHRUS_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -180,6 +180,31 @@ int orthrus_argmax(const void *logits, int64_t rows, int V, int dtype,
 size_t orthrus_argmax_workspace_bytes(int64_t rows, int V, int dtype);
 
 /*
+ * orthrus_lmhead_argmax -- greedy prediction straight from hidden states
+ * (summary §2.3: both views predict greedily; the consensus compares their
+ * argmax tokens): idx[r] = argmax_v sum_k hidden[r][k] * weight[v][k], lowest
+ * index on ties, without materialising the R x V logits.  bf16 inputs, fp32
+ * accumulation.
+ *
+ *  hidden    [R][H] bf16, 16-byte aligned (final hidden states of R rows,
+ *            e.g. the B*K block rows of one view)
+ *  weight    [V][H] bf16, 16-byte aligned (the LM head, one row per token)
+ *  idx       out int32 [R]
+ *  workspace >= orthrus_lmhead_argmax_workspace_bytes(R, H, V, dtype) bytes
+ *            (8-byte aligned); contents on entry are ignored.
+ *  dtype must be BF16 (F32 -> ORTHRUS_ERR_UNSUPPORTED); H a multiple of 128,
+ *  128 <= H <= 65536; 1 <= R <= 2,097,120; V >= 1.  The weight matrix is read
+ *  once per 32 rows, so the call suits decode-sized R.  The argmax decision
+ *  is taken on the fp32 accumulations: logits within a few fp32 ulps of each
+ *  other may resolve differently from an exact evaluation.
+ */
+int orthrus_lmhead_argmax(const void *hidden, const void *weight, int R, int H,
+                          int V, int dtype, int32_t *idx, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+size_t orthrus_lmhead_argmax_workspace_bytes(int R, int H, int V, int dtype);
+
+/*
  * orthrus_kv_append -- commit (summary §2.3 step 3; agents-report core
  * design: accepted tokens' KV state is appended to the shared cache).
  *

@@ -12,6 +12,9 @@ of the pages it follows (see the C file's header for the source list):
   or causal (AR verification) inside the block; summary §2.1-§2.3.
 * ``argmax_rows`` -- greedy prediction per row, lowest index on ties;
   summary §2.3 step 3.
+* ``lmhead_logits`` / ``lmhead_argmax`` -- the greedy prediction from final
+  hidden states (logits = hidden . W^T in fp64, then ``argmax_rows``);
+  summary §2.3.
 * ``consensus``   -- left-to-right exact consensus; summary §2.3 step 3.
 * ``kv_append``   -- commit of the accepted rows' KV; summary §2.3 step 3 and
   the agents-report core-design section.
@@ -125,6 +128,26 @@ def argmax_rows(x):
     if _load().oracle_argmax_rows(_ptr(x), rows, V, _ptr(idx)) != 0:
         raise ValueError("argmax undefined: NaN in logits")
     return idx.reshape(x.shape[:-1])
+
+
+def lmhead_logits(hidden, weight, chunk: int = 8192):
+    """fp64 logits hidden [R, H] . weight[V, H]^T -> [R, V] (a library matmul
+    per block of vocabulary rows, so that weight never exists whole in fp64)."""
+    def f64(a):   # numpy, or a tensor-like with .double().numpy() (bf16 inputs)
+        return _f64(a.double().numpy() if hasattr(a, "double") else a)
+    h = f64(hidden)
+    R, H = h.shape
+    V = weight.shape[0]
+    out = np.empty((R, V), np.float64)
+    for v0 in range(0, V, chunk):
+        w = f64(weight[v0:v0 + chunk])
+        out[:, v0:v0 + w.shape[0]] = h @ w.T
+    return out
+
+
+def lmhead_argmax(hidden, weight):
+    """Greedy tokens: argmax_v of the fp64 logits, lowest index on ties."""
+    return argmax_rows(lmhead_logits(hidden, weight))
 
 
 def consensus(d_tok, a_tok):

@@ -32,7 +32,7 @@ def attn(c, **kw):
 
 def test_exports_every_declared_function():
     declared = B.header_functions()
-    assert len(declared) == 9
+    assert len(declared) == 11
     for name in declared:
         assert hasattr(B.lib(), name), name
     assert set(declared) == set(B.SIGNATURES)
@@ -145,6 +145,34 @@ def test_consensus_validation_and_workspace():
     assert f(*bad, FAKE, need, None) == B.ERR_SHAPE
     assert B.orthrus_argmax_workspace_bytes(10, 1000, B.F32) == 10 * 1 * 8
     assert B.lib().orthrus_argmax(FAKE, 0, 10, B.F32, FAKE, FAKE, 8, None) == B.ERR_SHAPE
+
+
+def test_lmhead_argmax_validation_and_workspace():
+    f = B.lib().orthrus_lmhead_argmax
+    ws_bytes = B.orthrus_lmhead_argmax_workspace_bytes
+    # R rows x ceil(V / 128) vocabulary blocks of 64-bit keys
+    assert ws_bytes(32, 4096, 151936, B.BF16) == 32 * 1187 * 8
+    assert ws_bytes(1, 128, 1, B.BF16) == 8
+    assert ws_bytes(32, 4096, 151936, B.F32) == 0        # bf16 only
+    assert ws_bytes(32, 100, 1000, B.BF16) == 0          # H not a multiple of 128
+    need = ws_bytes(32, 4096, 151936, B.BF16)
+
+    def call(hidden=FAKE, weight=FAKE, R=32, H=4096, V=151936, dtype=B.BF16, idx=FAKE, ws=FAKE,
+             wsb=need):
+        return f(hidden, weight, R, H, V, dtype, idx, ws, wsb, None)
+
+    assert call(hidden=None) == B.ERR_NULL
+    assert call(weight=None) == B.ERR_NULL
+    assert call(idx=None) == B.ERR_NULL
+    assert call(dtype=7) == B.ERR_DTYPE
+    assert call(R=0) == B.ERR_SHAPE
+    assert call(V=0) == B.ERR_SHAPE
+    assert call(dtype=B.F32) == B.ERR_UNSUPPORTED
+    assert call(H=4000) == B.ERR_UNSUPPORTED
+    assert call(H=64) == B.ERR_UNSUPPORTED
+    assert call(hidden=FAKE + 2) == B.ERR_UNSUPPORTED      # misaligned
+    assert call(ws=None) == B.ERR_WORKSPACE
+    assert call(wsb=need - 1) == B.ERR_WORKSPACE
 
 
 def test_kv_append_validation():

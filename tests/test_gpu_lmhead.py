@@ -1,0 +1,89 @@
+"""Greedy prediction from hidden states on the GPU (orthrus_lmhead_argmax)
+against the fp64 oracle.  The kernel decides the argmax on fp32
+accumulations, so where the oracle's best two logits are closer than the
+fp32 accumulation bound either index is a valid answer: rows are compared
+exactly when the gap exceeds the bound, and otherwise the GPU's choice must
+lie within the bound of the maximum."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from ar_shared_kv_amd import api
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (name, R, H, V)
+    ("qwen3-vocab", 32, 1024, 151936),
+    ("deep-H-ragged-V", 7, 4096, 1000),
+    ("three-row-blocks", 70, 256, 130),
+    ("one-row-one-block", 1, 128, 1),
+]
+
+
+def check(name, h, w, got):
+    logits = oracle.lmhead_logits(h, w)
+    ref = oracle.argmax_rows(logits)
+    H = h.shape[1]
+    # fp32 accumulation bound per row: H * 2^-24 * sum_k |x_k w_vk|, over v
+    mag = np.abs(h.double().numpy()) @ np.abs(w.double().numpy()).T
+    bound = 2.0 * H * 2.0 ** -24 * mag.max(axis=1)
+    exact = 0
+    for r in range(len(ref)):
+        top = np.sort(logits[r])[-2:] if logits.shape[1] > 1 else np.array([-np.inf, logits[r, 0]])
+        if top[1] - top[0] > 2 * bound[r]:
+            assert got[r] == ref[r], f"{name} row {r}: {got[r]} vs {ref[r]} (clear gap)"
+            exact += 1
+        else:
+            assert logits[r, got[r]] >= logits[r, ref[r]] - 2 * bound[r], f"{name} row {r}"
+    say(f"  {name}: {exact}/{len(ref)} rows with a clear gap, all equal")
+    return exact
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_lmhead_argmax_matches_oracle(case):
+    name, R, H, V = case
+    h, w = W.lmhead_inputs(R, H, V, seed=R)
+    say(f"lmhead {name} R={R} H={H} V={V}")
+    got = api.lmhead_argmax(h.cuda(), w.cuda()).cpu().numpy()
+    exact = check(name, h, w, got)
+    assert exact >= R // 2
+
+
+def test_lmhead_argmax_duplicate_rows_take_the_lowest_index():
+    R, H, V = 4, 512, 3000
+    h, w = W.lmhead_inputs(R, H, V, seed=11)
+    # rows 2900 and 333 are the same vector, aligned with hidden row 0: for
+    # row 0 they carry bitwise-equal fp32 logits, the largest of the row
+    best = (h[0].float() / h[0].float().norm()).to(torch.bfloat16)
+    w[2900] = best
+    w[333] = best
+    got = api.lmhead_argmax(h.cuda(), w.cuda()).cpu().numpy()
+    assert got[0] == 333
+    check("duplicates", h, w, got)
+
+
+def test_lmhead_argmax_graph_replay_equals_eager():
+    R, H, V = 32, 1024, 20000
+    h, w = W.lmhead_inputs(R, H, V, seed=5)
+    hd, wd = h.cuda(), w.cuda()
+    idx = torch.empty(R, dtype=torch.int32, device="cuda")
+    from ar_shared_kv_amd import _binding as B_
+    n = B_.orthrus_lmhead_argmax_workspace_bytes(R, H, V, B_.BF16)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    api.lmhead_argmax(hd, wd, idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    ref = idx.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.lmhead_argmax(hd, wd, idx=idx, workspace=ws)
+    for _ in range(3):
+        idx.fill_(-1)
+        ws.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref)

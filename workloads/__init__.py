@@ -229,6 +229,20 @@ def step_inputs(cfg: Config, layers: int | None = None, salt: int = 0,
     return StepInputs(cfg, lens, table, num_pages, capacity, lay, diff, ar)
 
 
+T_LM_HIDDEN, T_LM_WEIGHT = 13, 14
+
+
+def lmhead_inputs(R: int, H: int, V: int, seed: int = 0):
+    """Hidden states [R, H] and an LM-head weight [V, H], bf16.
+
+    The hidden rows are N(0,1); the weight rows N(0,1)/sqrt(H), so that the
+    logits are N(0,1)-scaled like a trained head's, with no structure."""
+    hidden = normal((R, H), torch.bfloat16, 1000 * 90 + T_LM_HIDDEN + 100000 * seed)
+    w = torch.randn((V, H), generator=gen(1000 * 90 + T_LM_WEIGHT + 100000 * seed),
+                    dtype=torch.float32)
+    return hidden, (w * H ** -0.5).to(torch.bfloat16)
+
+
 def custom_step(B: int, Hq: int, Hkv: int, D: int, K: int, lens, dtype=BF16, paged=False,
                 seed: int = 0, V: int = 1000, p=0.8, extra_capacity: int = 0) -> StepInputs:
     """A small step with explicit per-request prefix lengths (edge cases).

@@ -9,13 +9,14 @@
 // Design (MI355X): decode has few rows (R = B*K, 32 at the Qwen3-8B shape)
 // against V = 151,936 vocabulary rows, so the weight matrix is read once and
 // the work is HBM-bound.  One work-group per (128 vocabulary rows, 32 hidden
-// rows): 128 x 128 weight chunks and the matching 32 x 128 hidden chunk
-// stream HBM -> LDS with global_load_lds (16-byte granules XOR-swizzled per
-// row), two chunks in flight per CU (two work-groups of a 2-slot ring each).
-// Each wave owns 32 vocabulary rows: logits^T = W x^T on the matrix cores
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation over H), then a (value,
-// lowest index) key per hidden row is reduced over the lanes, the waves and,
-// in a second launch, over the vocabulary blocks.
+// rows): 128 x 64 weight chunks and the matching 32 x 64 hidden chunk stream
+// HBM -> LDS with global_load_lds (16-byte granules XOR-swizzled per row)
+// through a 3-slot ring, two chunks in flight while one is computed; two
+// work-groups share a CU (61 KiB of LDS each).  Each wave owns 32 vocabulary
+// rows: logits^T = W x^T on the matrix cores (v_mfma_f32_32x32x16_bf16, fp32
+// accumulation over H), then a (value, lowest index) key per hidden row is
+// reduced over the lanes, the waves and, in a second launch with one
+// work-group per row, over the vocabulary blocks.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,13 +27,9 @@ namespace orthrus {
 namespace {
 
 constexpr int kLmVB = 128;                    // vocabulary rows per work-group
-constexpr int kLmHC = 128;                    // hidden columns per chunk
 constexpr int kLmRB = 32;                     // hidden rows per work-group
-constexpr int kLmWBytes = kLmVB * kLmHC * 2;  // 32 KiB of weights per chunk
-constexpr int kLmXBytes = kLmRB * kLmHC * 2;  // 8 KiB of hidden states per chunk
-constexpr int kLmSlot = kLmWBytes + kLmXBytes;
-constexpr int kLmStages = 2;
-constexpr int kLmLoads = (kLmWBytes + kLmXBytes) / (256 * 16);   // DMA loads per lane per chunk
+constexpr int kLmHC = 64;                     // hidden columns per chunk (the H granularity)
+constexpr int kLmStages = 3;                  // ring slots: two chunks in flight per work-group
 
 // 16-byte global -> LDS copy per lane (lane l lands at lds + 16*l); the waits
 // are the explicit s_waitcnt of the chunk loop.
@@ -44,11 +41,23 @@ __device__ __forceinline__ void lm_dma16(const void* gptr, uint32_t lds_addr) {
                  : "memory", "m0");
 }
 
+// HC hidden columns per chunk, NSTAGE ring slots (NSTAGE - 1 chunks in flight
+// while one is computed).
+template <int HC, int NSTAGE>
 __global__ void __launch_bounds__(256, 2)
 lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int R, int H,
                      int V, int nvb, uint64_t* __restrict__ ws)
 {
-    __shared__ __attribute__((aligned(1024))) char smem[kLmStages * kLmSlot];
+    constexpr int WB = kLmVB * HC * 2;          // weight bytes per chunk
+    constexpr int XB = kLmRB * HC * 2;          // hidden bytes per chunk
+    constexpr int SLOT = WB + XB;
+    constexpr int GR = HC / 8;                  // 16-byte granules per row
+    constexpr int RPP = 1024 / (HC * 2);        // rows per 1 KiB wave load
+    constexpr int LOADS = SLOT / 4096;          // loads per lane per chunk
+    constexpr int NPRE = NSTAGE - 1;
+    static_assert(SLOT % 4096 == 0 && WB % 1024 == 0, "whole wave loads per chunk");
+    static_assert(LOADS * NSTAGE <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * SLOT];
     __shared__ uint64_t red[4][32];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -57,22 +66,22 @@ lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict_
     const int vb = blockIdx.x;
     const int v0 = vb * kLmVB;
     const int r0 = blockIdx.y * kLmRB;
-    const int nchunk = H / kLmHC;
+    const int nchunk = H / HC;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(ORTHRUS_LDS void*)&smem[0];
 
-    // DMA of chunk c into slot c % 2.  A 1 KiB wave load covers 4 rows of
-    // 16 granules; lane l writes LDS granule l % 16 of row 4k + l / 16 with the
-    // global granule (l % 16) ^ (row % 16), so that granule g of a row sits at
-    // g ^ (row % 16) and the fragment reads below hit distinct banks.
+    // DMA of chunk c into slot c % NSTAGE.  A 1 KiB wave load covers RPP rows
+    // of GR granules; lane l writes LDS granule l % GR of its row with the
+    // global granule (l % GR) ^ (row % GR), so that granule g of a row sits at
+    // g ^ (row % GR) and the fragment reads below spread over the banks.
     auto issue = [&](int c) __attribute__((always_inline)) {
-        const uint32_t slot = lds_base + (uint32_t)((c % kLmStages) * kLmSlot);
-        const int col = c * kLmHC;
+        const uint32_t slot = lds_base + (uint32_t)((c % NSTAGE) * SLOT);
+        const int col = c * HC;
 #pragma unroll
-        for (int i = 0; i < kLmLoads; ++i) {
+        for (int i = 0; i < LOADS; ++i) {
             const int k = i * 4 + wave;                  // 1 KiB piece of the slot
-            const bool isx = k >= kLmWBytes / 1024;
-            const int row = (isx ? k - kLmWBytes / 1024 : k) * 4 + lane / 16;
-            const int gsrc = (lane % 16) ^ (row % 16);
+            const bool isx = k >= WB / 1024;
+            const int row = (isx ? k - WB / 1024 : k) * RPP + lane / GR;
+            const int gsrc = (lane % GR) ^ (row % GR);
             const uint16_t* src;
             if (isx) {
                 const int rr = r0 + row < R ? r0 + row : R - 1;
@@ -84,26 +93,39 @@ lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict_
             lm_dma16(src, slot + (uint32_t)(k * 1024));
         }
     };
+    // wait until chunk c has landed: at most min(NPRE - 1, chunks after c)
+    // later chunks of this lane may still fly
+    auto wait_chunk = [&](int c) __attribute__((always_inline)) {
+        const int later = nchunk - 1 - c;
+        const int pend = later < NPRE - 1 ? later : NPRE - 1;
+        switch (pend) {
+            case 0: __builtin_amdgcn_s_waitcnt(vmcnt_encode(0)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(vmcnt_encode(LOADS)); break;
+            case 2: __builtin_amdgcn_s_waitcnt(vmcnt_encode(2 * LOADS)); break;
+            default: __builtin_amdgcn_s_waitcnt(vmcnt_encode(3 * LOADS)); break;
+        }
+    };
+    static_assert(NPRE - 1 <= 3, "wait_chunk covers up to 3 later chunks");
 
     f32x16 acc = f32x16{};
     const int vrow = wave * 32 + (lane & 31);            // this lane's vocabulary row (A operand)
     const int xrow = lane & 31;                          // this lane's hidden row (B operand)
-    issue(0);
+    for (int c = 0; c < NPRE && c < nchunk; ++c) issue(c);
     for (int c = 0; c < nchunk; ++c) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));     // chunk c landed (this lane's part)
-        __syncthreads();                                 // ... everyone's; slot (c+1)%2 is free
-        if (c + 1 < nchunk) issue(c + 1);
-        const char* Ws = smem + (c % kLmStages) * kLmSlot;
-        const char* Xs = Ws + kLmWBytes;
-        u32x4 af[kLmHC / 16], bfr[kLmHC / 16];
+        wait_chunk(c);
+        __syncthreads();                 // everyone's part landed; slot (c-1) % NSTAGE is free
+        if (c + NPRE < nchunk) issue(c + NPRE);
+        const char* Ws = smem + (c % NSTAGE) * SLOT;
+        const char* Xs = Ws + WB;
+        u32x4 af[HC / 16], bfr[HC / 16];
 #pragma unroll
-        for (int ds = 0; ds < kLmHC / 16; ++ds) {
+        for (int ds = 0; ds < HC / 16; ++ds) {
             const int g = 2 * ds + half;
-            af[ds] = *(const u32x4*)(Ws + vrow * (kLmHC * 2) + ((g ^ (vrow % 16)) * 16));
-            bfr[ds] = *(const u32x4*)(Xs + xrow * (kLmHC * 2) + ((g ^ (xrow % 16)) * 16));
+            af[ds] = *(const u32x4*)(Ws + vrow * (HC * 2) + ((g ^ (vrow % GR)) * 16));
+            bfr[ds] = *(const u32x4*)(Xs + xrow * (HC * 2) + ((g ^ (xrow % GR)) * 16));
         }
 #pragma unroll
-        for (int ds = 0; ds < kLmHC / 16; ++ds)
+        for (int ds = 0; ds < HC / 16; ++ds)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[ds]),
                                                           __builtin_bit_cast(bf16x8, bfr[ds]),
                                                           acc, 0, 0, 0);
@@ -132,10 +154,38 @@ lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict_
     }
 }
 
+// Second pass: one work-group per hidden row reduces that row's per-block
+// keys.  Every lane issues all its loads before the first comparison, so the
+// pass costs one memory round trip for up to 2048 vocabulary blocks.
+__global__ void __launch_bounds__(256)
+lmhead_finalize_kernel(const uint64_t* __restrict__ ws, int nvb, int32_t* __restrict__ idx)
+{
+    __shared__ uint64_t part[4];
+    const uint64_t* p = ws + (int64_t)blockIdx.x * nvb;
+    uint64_t key = 0;
+    for (int c0 = threadIdx.x; c0 < nvb; c0 += 256 * 8) {
+        uint64_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = c0 + 256 * j < nvb ? p[c0 + 256 * j] : 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) key = v[j] > key ? v[j] : key;
+    }
+    key = wave_max_u64(key);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = key;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t k = part[0];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) k = part[q] > k ? part[q] : k;
+        idx[blockIdx.x] = (int32_t)argmax_key_index(k);
+    }
+}
+
 int64_t lm_blocks(int V) { return ((int64_t)V + kLmVB - 1) / kLmVB; }
 
 bool lm_shape_ok(int R, int H, int V) {
-    return R >= 1 && R <= 65535 * kLmRB && H >= kLmHC && H % kLmHC == 0 && H <= 65536 && V >= 1;
+    return R >= 1 && R <= 65535 * kLmRB && H >= kLmHC && H % kLmHC == 0 && H <= 65536 &&
+           V >= 1;
 }
 
 }  // namespace
@@ -168,12 +218,13 @@ int orthrus_lmhead_argmax(const void *hidden, const void *weight, int R, int H, 
         return ORTHRUS_ERR_WORKSPACE;
     uint64_t *ws = static_cast<uint64_t *>(workspace);
     const dim3 grid((unsigned)nvb, (unsigned)((R + kLmRB - 1) / kLmRB));
-    hipLaunchKernelGGL(lmhead_argmax_kernel, grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, kLmStages>), grid, dim3(256), 0, stream,
                        static_cast<const uint16_t *>(hidden), static_cast<const uint16_t *>(weight),
                        R, H, V, (int)nvb, ws);
     if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
-    return launch_argmax_finalize(ws, R, (int)nvb, idx, stream) == hipSuccess ? ORTHRUS_OK
-                                                                               : ORTHRUS_ERR_LAUNCH;
+    hipLaunchKernelGGL(lmhead_finalize_kernel, dim3((unsigned)R), dim3(256), 0, stream,
+                       static_cast<const uint64_t *>(ws), (int)nvb, idx);
+    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }
 
 }  // extern "C"

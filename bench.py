@@ -35,21 +35,24 @@ HBM_PEAK_GBPS = 8000.0
 # sources that decide what the block-attention launch does (kernel and plan)
 ATTN_SOURCES = ("ar_shared_kv_amd/csrc/block_attn.hip", "ar_shared_kv_amd/csrc/kernels.hpp",
                 "ar_shared_kv_amd/csrc/common.hpp", "ar_shared_kv_amd/csrc/abi.cpp")
+# ... and what the fused LM-head argmax call does
+LM_SOURCES = ("ar_shared_kv_amd/csrc/lmhead.hip", "ar_shared_kv_amd/csrc/common.hpp")
 
 
-def attn_source_hash():
+def attn_source_hash(sources=ATTN_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for f in ATTN_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, splits):
-    """HBM bytes per block-attention launch from the committed counter summary
-    of this workload, or None when the kernel sources changed since then."""
-    path = os.path.join(ROOT, "profiles", f"block_attn_{workload}_traffic.txt")
+def measured_traffic(workload, splits, name=None, sources=ATTN_SOURCES):
+    """HBM bytes per block-attention launch (or per call of the profile `name`)
+    from the committed counter summary of this workload, or None when the
+    kernel sources changed since then."""
+    path = os.path.join(ROOT, "profiles", name or f"block_attn_{workload}_traffic.txt")
     if splits or not os.path.exists(path):
         return None
     fields = {}
@@ -58,7 +61,7 @@ def measured_traffic(workload, splits):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("source_hash") != attn_source_hash():
+    if fields.get("source_hash") != attn_source_hash(sources):
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -76,6 +79,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets cycled by consecutive steps (0 = enough for 512 MiB)")
+    ap.add_argument("--lmhead", action="store_true",
+                    help="time the fused LM-head argmax (greedy tokens from hidden states) at "
+                         "the Qwen3-8B head shape instead of the decode step")
     ap.add_argument("--calib-bytes", type=int, default=0,
                     help="first run one plain device copy of this many bytes (a known-size "
                          "kernel for scaling hardware byte counters)")
@@ -283,6 +289,71 @@ def torch_int(t):
     return torch.int16 if t.element_size() == 2 else torch.int32
 
 
+def calibrate(nbytes):
+    """An elementwise kernel that reads and writes nbytes once each: the
+    yardstick that scales the HBM byte counters."""
+    if not nbytes:
+        return
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def lmhead_main(args):
+    """The fused LM-head argmax at the Qwen3-8B head shape: R = B*K = 32 hidden
+    rows of H = 4,096 against V = 151,936 vocabulary rows, one view per call.
+    Algorithmic bytes: the weight, the hidden rows and the tokens, once."""
+    import torch
+    import workloads as W
+    from ar_shared_kv_amd import api
+    from ar_shared_kv_amd import _binding as B_
+    R, H, V = 32, 4096, 151936
+    calibrate(args.calib_bytes)
+    h, w = W.lmhead_inputs(R, H, V, seed=0)
+    hd, wd = h.cuda(), w.cuda()
+    idx = torch.empty(R, dtype=torch.int32, device="cuda")
+    n = B_.orthrus_lmhead_argmax_workspace_bytes(R, H, V, B_.BF16)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    call = lambda: api.lmhead_argmax(hd, wd, idx=idx, workspace=ws)
+    ms, _ = timed(call, args.steps, args.warmup, not args.no_graph)
+    nbytes = V * H * 2 + R * H * 2 + R * 4
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    flops = 2 * R * H * V
+    res = {
+        "metric": "fused LM-head argmax calls/s (greedy tokens of one view's 32 block rows)",
+        "value": round(1e3 / ms, 3), "unit": "calls/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3-8b-lmhead", "R": R, "H": H, "V": V,
+                   "graph": not args.no_graph},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("qwen3-8b-lmhead", 0,
+                                                 "lmhead_argmax_qwen3-8b_traffic.txt", LM_SOURCES),
+                     "kernel": "lmhead_argmax_kernel + lmhead_finalize_kernel, per call",
+                     "us_per_launch": round(ms * 1e3, 3), "bytes_per_launch": nbytes,
+                     "mfma_frac": round(flops / (ms * 1e-3) / 2.5e15, 4)},
+    }
+    if not args.no_cpu:
+        import oracle
+        # the oracle's fp64 logits over a sample of vocabulary rows, scaled to V
+        vs = V // 16
+        t0 = time.perf_counter()
+        oracle.lmhead_argmax(h, w[:vs])
+        t = (time.perf_counter() - t0) * V / vs
+        from threadpoolctl import threadpool_info
+        blas = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        res["cpu_baseline"] = {"value": round(1.0 / t, 4), "unit": "calls/s",
+                               "cores": max(blas) if blas else 1, "kind": "oracle",
+                               "sample": f"fp64 logits + argmax over {vs} of {V} vocabulary rows, "
+                                         "scaled to the whole head"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -292,19 +363,15 @@ def main():
     import torch
     import workloads as W
     assert torch.cuda.is_available(), "needs a GPU"
+    if args.lmhead:
+        lmhead_main(args)
+        return
     cfg = W.CONFIGS[args.config]
     if args.K:
         cfg = cfg.with_(K=args.K)
     splits = args.splits or cfg.num_splits
     log(f"workload {cfg.name} K={cfg.K} splits={splits or 'auto'}")
-    if args.calib_bytes:
-        # an elementwise kernel that reads and writes calib_bytes once each
-        src = torch.ones(args.calib_bytes // 4, dtype=torch.int32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.bitwise_not(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    calibrate(args.calib_bytes)
     step = Step(cfg, splits, args.sets)
     graph = not args.no_graph
 

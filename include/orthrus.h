@@ -192,8 +192,8 @@ size_t orthrus_argmax_workspace_bytes(int64_t rows, int V, int dtype);
  *  idx       out int32 [R]
  *  workspace >= orthrus_lmhead_argmax_workspace_bytes(R, H, V, dtype) bytes
  *            (8-byte aligned); contents on entry are ignored.
- *  dtype must be BF16 (F32 -> ORTHRUS_ERR_UNSUPPORTED); H a multiple of 128,
- *  128 <= H <= 65536; 1 <= R <= 2,097,120; V >= 1.  The weight matrix is read
+ *  dtype must be BF16 (F32 -> ORTHRUS_ERR_UNSUPPORTED); H a multiple of 64,
+ *  64 <= H <= 65536; 1 <= R <= 2,097,120; V >= 1.  The weight matrix is read
  *  once per 32 rows, so the call suits decode-sized R.  The argmax decision
  *  is taken on the fp32 accumulations: logits within a few fp32 ulps of each
  *  other may resolve differently from an exact evaluation.

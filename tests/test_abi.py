@@ -169,7 +169,8 @@ def test_lmhead_argmax_validation_and_workspace():
     assert call(V=0) == B.ERR_SHAPE
     assert call(dtype=B.F32) == B.ERR_UNSUPPORTED
     assert call(H=4000) == B.ERR_UNSUPPORTED
-    assert call(H=64) == B.ERR_UNSUPPORTED
+    assert call(H=96) == B.ERR_UNSUPPORTED
+    assert call(H=32) == B.ERR_UNSUPPORTED
     assert call(hidden=FAKE + 2) == B.ERR_UNSUPPORTED      # misaligned
     assert call(ws=None) == B.ERR_WORKSPACE
     assert call(wsb=need - 1) == B.ERR_WORKSPACE

@@ -21,6 +21,7 @@ CASES = [
     ("deep-H-ragged-V", 7, 4096, 1000),
     ("three-row-blocks", 70, 256, 130),
     ("one-row-one-block", 1, 128, 1),
+    ("one-chunk-H64", 5, 64, 300),
 ]
 
 

@@ -196,7 +196,10 @@ size_t orthrus_argmax_workspace_bytes(int64_t rows, int V, int dtype);
  *  64 <= H <= 65536; 1 <= R <= 2,097,120; V >= 1.  The weight matrix is read
  *  once per 32 rows, so the call suits decode-sized R.  The argmax decision
  *  is taken on the fp32 accumulations: logits within a few fp32 ulps of each
- *  other may resolve differently from an exact evaluation.
+ *  other may resolve differently from an exact evaluation.  Equal fp32
+ *  logits go to the lowest index; the accumulation order over H is the same
+ *  within each block of 128 vocabulary rows and rotates from block to block,
+ *  so equal weight rows give bitwise-equal logits only inside one block.
  */
 int orthrus_lmhead_argmax(const void *hidden, const void *weight, int R, int H,
                           int V, int dtype, int32_t *idx, void *workspace,

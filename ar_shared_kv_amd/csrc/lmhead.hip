@@ -8,12 +8,13 @@
 //
 // Design (MI355X): decode has few rows (R = B*K, 32 at the Qwen3-8B shape)
 // against V = 151,936 vocabulary rows, so the weight matrix is read once and
-// the work is HBM-bound.  One work-group per (128 vocabulary rows, 32 hidden
-// rows): 128 x 64 weight chunks and the matching 32 x 64 hidden chunk stream
-// HBM -> LDS with global_load_lds (16-byte granules XOR-swizzled per row)
-// through a 3-slot ring, two chunks in flight while one is computed; two
-// work-groups share a CU (61 KiB of LDS each).  Each wave owns 32 vocabulary
-// rows: logits^T = W x^T on the matrix cores (v_mfma_f32_32x32x16_bf16, fp32
+// the work is HBM-bound.  One work-group per (128 vocabulary rows, RB hidden
+// rows; RB = 32, 64 or 128 by R, so that serving batches read the weight once
+// per 128 rows): 128 x 64 weight chunks and the matching RB x 64 hidden chunk
+// stream HBM -> LDS with global_load_lds (16-byte granules XOR-swizzled per
+// row) through a 3-slot ring, two chunks in flight while one is computed; at
+// RB <= 64 two work-groups share a CU.  Each wave owns 32 vocabulary rows:
+// logits^T = W x^T on the matrix cores (v_mfma_f32_32x32x16_bf16, fp32
 // accumulation over H, each block starting at its own column chunk), then a
 // (value, lowest index) key per hidden row is reduced over the lanes, the
 // waves and, in a second launch with one work-group per row, over the
@@ -28,7 +29,6 @@ namespace orthrus {
 namespace {
 
 constexpr int kLmVB = 128;                    // vocabulary rows per work-group
-constexpr int kLmRB = 32;                     // hidden rows per work-group
 constexpr int kLmHC = 64;                     // hidden columns per chunk (the H granularity)
 constexpr int kLmStages = 3;                  // ring slots: two chunks in flight per work-group
 
@@ -43,14 +43,16 @@ __device__ __forceinline__ void lm_dma16(const void* gptr, uint32_t lds_addr) {
 }
 
 // HC hidden columns per chunk, NSTAGE ring slots (NSTAGE - 1 chunks in flight
-// while one is computed).
-template <int HC, int NSTAGE>
+// while one is computed), RB hidden rows per work-group (32, 64 or 128: the
+// weight is read once per RB rows).
+template <int HC, int NSTAGE, int RB>
 __global__ void __launch_bounds__(256, 2)
 lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int R, int H,
                      int V, int nvb, uint64_t* __restrict__ ws)
 {
     constexpr int WB = kLmVB * HC * 2;          // weight bytes per chunk
-    constexpr int XB = kLmRB * HC * 2;          // hidden bytes per chunk
+    constexpr int XB = RB * HC * 2;             // hidden bytes per chunk
+    constexpr int NB = RB / 32;                 // 32-row MFMA column blocks per wave
     constexpr int SLOT = WB + XB;
     constexpr int GR = HC / 8;                  // 16-byte granules per row
     constexpr int RPP = 1024 / (HC * 2);        // rows per 1 KiB wave load
@@ -59,14 +61,14 @@ lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict_
     static_assert(SLOT % 4096 == 0 && WB % 1024 == 0, "whole wave loads per chunk");
     static_assert(LOADS * NSTAGE <= 63, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * SLOT];
-    __shared__ uint64_t red[4][32];
+    __shared__ uint64_t red[4][RB];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int half = lane >> 5;
     const int vb = blockIdx.x;
     const int v0 = vb * kLmVB;
-    const int r0 = blockIdx.y * kLmRB;
+    const int r0 = blockIdx.y * RB;
     const int nchunk = H / HC;
     // The walk over H starts at chunk vb mod nchunk and wraps.  Weight rows
     // are H*2 bytes apart, so work-groups that all read the same column chunk
@@ -115,9 +117,10 @@ lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict_
     };
     static_assert(NPRE - 1 <= 3, "wait_chunk covers up to 3 later chunks");
 
-    f32x16 acc = f32x16{};
+    f32x16 acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = f32x16{};
     const int vrow = wave * 32 + (lane & 31);            // this lane's vocabulary row (A operand)
-    const int xrow = lane & 31;                          // this lane's hidden row (B operand)
     for (int c = 0; c < NPRE && c < nchunk; ++c) issue(c);
     for (int c = 0; c < nchunk; ++c) {
         wait_chunk(c);
@@ -125,36 +128,45 @@ lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict_
         if (c + NPRE < nchunk) issue(c + NPRE);
         const char* Ws = smem + (c % NSTAGE) * SLOT;
         const char* Xs = Ws + WB;
-        u32x4 af[HC / 16], bfr[HC / 16];
+        u32x4 af[HC / 16], bfr[NB][HC / 16];
 #pragma unroll
         for (int ds = 0; ds < HC / 16; ++ds) {
             const int g = 2 * ds + half;
             af[ds] = *(const u32x4*)(Ws + vrow * (HC * 2) + ((g ^ (vrow % GR)) * 16));
-            bfr[ds] = *(const u32x4*)(Xs + xrow * (HC * 2) + ((g ^ (xrow % GR)) * 16));
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int xrow = 32 * j + (lane & 31);   // hidden row of block j (B operand)
+                bfr[j][ds] = *(const u32x4*)(Xs + xrow * (HC * 2) + ((g ^ (xrow % GR)) * 16));
+            }
         }
 #pragma unroll
         for (int ds = 0; ds < HC / 16; ++ds)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[ds]),
-                                                          __builtin_bit_cast(bf16x8, bfr[ds]),
-                                                          acc, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, af[ds]), __builtin_bit_cast(bf16x8, bfr[j][ds]),
+                    acc[j], 0, 0, 0);
     }
 
-    // acc[i] = logit of vocabulary row v0 + 32*wave + 8*(i/4) + 4*half + i%4
-    // for hidden row r0 + lane%32
-    uint64_t key = 0;
+    // acc[j][i] = logit of vocabulary row v0 + 32*wave + 8*(i/4) + 4*half + i%4
+    // for hidden row r0 + 32*j + lane%32
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int v = v0 + wave * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (v < V) {
-            const uint64_t k = argmax_key(acc[i], (uint32_t)v);
-            key = k > key ? k : key;
+    for (int j = 0; j < NB; ++j) {
+        uint64_t key = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int v = v0 + wave * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (v < V) {
+                const uint64_t k = argmax_key(acc[j][i], (uint32_t)v);
+                key = k > key ? k : key;
+            }
         }
+        const uint64_t o = shfl_xor_u64(key, 32);
+        key = o > key ? o : key;
+        if (lane < 32) red[wave][32 * j + lane] = key;
     }
-    const uint64_t o = shfl_xor_u64(key, 32);
-    key = o > key ? o : key;
-    if (lane < 32) red[wave][lane] = key;
     __syncthreads();
-    if (tid < 32) {
+    if (tid < RB) {
         uint64_t k = red[0][tid];
 #pragma unroll
         for (int q = 1; q < 4; ++q) k = red[q][tid] > k ? red[q][tid] : k;
@@ -192,7 +204,7 @@ lmhead_finalize_kernel(const uint64_t* __restrict__ ws, int nvb, int32_t* __rest
 int64_t lm_blocks(int V) { return ((int64_t)V + kLmVB - 1) / kLmVB; }
 
 bool lm_shape_ok(int R, int H, int V) {
-    return R >= 1 && R <= 65535 * kLmRB && H >= kLmHC && H % kLmHC == 0 && H <= 65536 &&
+    return R >= 1 && R <= 65535 * 32 && H >= kLmHC && H % kLmHC == 0 && H <= 65536 &&
            V >= 1;
 }
 
@@ -225,10 +237,20 @@ int orthrus_lmhead_argmax(const void *hidden, const void *weight, int R, int H, 
     if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 7u))
         return ORTHRUS_ERR_WORKSPACE;
     uint64_t *ws = static_cast<uint64_t *>(workspace);
-    const dim3 grid((unsigned)nvb, (unsigned)((R + kLmRB - 1) / kLmRB));
-    hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, kLmStages>), grid, dim3(256), 0, stream,
-                       static_cast<const uint16_t *>(hidden), static_cast<const uint16_t *>(weight),
-                       R, H, V, (int)nvb, ws);
+    // hidden rows per work-group: the weight is read ceil(R / RB) times
+    const uint16_t *xp = static_cast<const uint16_t *>(hidden);
+    const uint16_t *wp = static_cast<const uint16_t *>(weight);
+    if (R <= 32) {
+        hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, kLmStages, 32>), dim3((unsigned)nvb, 1),
+                           dim3(256), 0, stream, xp, wp, R, H, V, (int)nvb, ws);
+    } else if (R <= 64) {
+        hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, kLmStages, 64>), dim3((unsigned)nvb, 1),
+                           dim3(256), 0, stream, xp, wp, R, H, V, (int)nvb, ws);
+    } else {
+        hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, kLmStages, 128>),
+                           dim3((unsigned)nvb, (unsigned)((R + 127) / 128)), dim3(256), 0, stream,
+                           xp, wp, R, H, V, (int)nvb, ws);
+    }
     if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
     hipLaunchKernelGGL(lmhead_finalize_kernel, dim3((unsigned)R), dim3(256), 0, stream,
                        static_cast<const uint64_t *>(ws), (int)nvb, idx);

@@ -19,7 +19,9 @@ CASES = [
     # (name, R, H, V)
     ("qwen3-vocab", 32, 1024, 151936),
     ("deep-H-ragged-V", 7, 4096, 1000),
-    ("three-row-blocks", 70, 256, 130),
+    ("seventy-rows-one-128-row-block", 70, 256, 130),
+    ("fifty-rows-64-row-block", 50, 512, 3000),
+    ("serving-rows-three-128-row-blocks", 300, 512, 5000),
     ("one-row-one-block", 1, 128, 1),
     ("one-chunk-H64", 5, 64, 300),
 ]

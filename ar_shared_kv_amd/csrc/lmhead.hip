@@ -12,8 +12,8 @@
 // rows; RB = 32, 64 or 128 by R, so that serving batches read the weight once
 // per 128 rows): 128 x 64 weight chunks and the matching RB x 64 hidden chunk
 // stream HBM -> LDS with global_load_lds (16-byte granules XOR-swizzled per
-// row) through a 3-slot ring, two chunks in flight while one is computed; at
-// RB <= 64 two work-groups share a CU.  Each wave owns 32 vocabulary rows:
+// row) through a ring (3 slots at RB <= 64: two chunks in flight while one is
+// computed; 2 slots at RB = 128); two work-groups share a CU.  Each wave owns 32 vocabulary rows:
 // logits^T = W x^T on the matrix cores (v_mfma_f32_32x32x16_bf16, fp32
 // accumulation over H, each block starting at its own column chunk), then a
 // (value, lowest index) key per hidden row is reduced over the lanes, the
@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kLmVB = 128;                    // vocabulary rows per work-group
 constexpr int kLmHC = 64;                     // hidden columns per chunk (the H granularity)
-constexpr int kLmStages = 3;                  // ring slots: two chunks in flight per work-group
+constexpr int kLmStages = 3;                  // ring slots at RB <= 64: two chunks in flight
 
 // 16-byte global -> LDS copy per lane (lane l lands at lds + 16*l); the waits
 // are the explicit s_waitcnt of the chunk loop.
@@ -247,7 +247,9 @@ int orthrus_lmhead_argmax(const void *hidden, const void *weight, int R, int H, 
         hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, kLmStages, 64>), dim3((unsigned)nvb, 1),
                            dim3(256), 0, stream, xp, wp, R, H, V, (int)nvb, ws);
     } else {
-        hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, kLmStages, 128>),
+        // two slots: two work-groups per CU (68 KiB of LDS each) beat one with
+        // three slots (R = 1024: 1.90 vs 2.13 ms per call)
+        hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, 2, 128>),
                            dim3((unsigned)nvb, (unsigned)((R + 127) / 128)), dim3(256), 0, stream,
                            xp, wp, R, H, V, (int)nvb, ws);
     }

@@ -194,7 +194,8 @@ size_t orthrus_argmax_workspace_bytes(int64_t rows, int V, int dtype);
  *            (8-byte aligned); contents on entry are ignored.
  *  dtype must be BF16 (F32 -> ORTHRUS_ERR_UNSUPPORTED); H a multiple of 64,
  *  64 <= H <= 65536; 1 <= R <= 2,097,120; V >= 1.  The weight matrix is read
- *  once per 32 rows, so the call suits decode-sized R.  The argmax decision
+ *  once for R <= 256 (once per 256 rows beyond), so the call suits decode and
+ *  serving batches; large R is bound by the matrix cores.  The argmax decision
  *  is taken on the fp32 accumulations: logits within a few fp32 ulps of each
  *  other may resolve differently from an exact evaluation.  Equal fp32
  *  logits go to the lowest index; the accumulation order over H is the same

@@ -21,7 +21,9 @@ CASES = [
     ("deep-H-ragged-V", 7, 4096, 1000),
     ("seventy-rows-one-128-row-block", 70, 256, 130),
     ("fifty-rows-64-row-block", 50, 512, 3000),
-    ("serving-rows-three-128-row-blocks", 300, 512, 5000),
+    ("hundred-rows-one-128-row-block", 100, 512, 2000),
+    ("129-rows-one-256-row-block", 129, 256, 700),
+    ("serving-rows-two-256-row-blocks", 300, 512, 5000),
     ("one-row-one-block", 1, 128, 1),
     ("one-chunk-H64", 5, 64, 300),
 ]

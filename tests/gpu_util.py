@@ -5,6 +5,8 @@ fp32 accumulation: max abs error <= 1e-2; fp32 inputs: <= 1e-5; tokens,
 counts and the appended cache: bit-exact)."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -101,27 +103,52 @@ def gpu_attn(step: W.StepInputs, layer: W.LayerInputs, view: str, num_splits=0, 
 
 def half_ulp(x: np.ndarray, dtype) -> np.ndarray:
     """Half a unit in the last place of the output dtype at |x| (the rounding
-    any output of that dtype carries; 8 significant bits for bf16)."""
+    any output of that dtype carries; 8 significant bits for bf16).  Printed
+    as a diagnostic only: the assertion is the plain max |err| bound."""
     if dtype == torch.float32:
         return np.zeros_like(x)
     e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
     return 2.0 ** (e - 8)
 
 
+# Per-case parity record: every attention comparison appends one JSON line
+# (case name, max |err|, error relative to max |O|, lse error, the bound) to
+# this file, so that the margins of a GPU run are kept with its outputs.
+RECORD = os.environ.get("ORTHRUS_PARITY_RECORD",
+                        os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                     "gpurun_out", "parity_cases.jsonl"))
+RESULTS: list = []
+
+
+def record(kind: str, what: str, **fields):
+    row = {"kind": kind, "case": what, **fields}
+    RESULTS.append(row)
+    try:
+        os.makedirs(os.path.dirname(RECORD), exist_ok=True)
+        with open(RECORD, "a") as fh:
+            fh.write(json.dumps(row) + "\n")
+    except OSError:
+        pass
+
+
 def assert_attn_close(out, lse, ref_out, ref_lse, dtype, what=""):
-    """max |out - ref| <= TOL + half an output ulp at |ref| (the bf16 output's
-    own round-to-nearest-even), plus the relative and lse guards."""
+    """max |out - ref| <= TOL (1e-2 for bf16 inputs, 1e-5 for fp32), plus the
+    relative and lse guards.  The error beyond the output's own rounding is
+    printed and recorded next to it."""
     o = f64(out)
-    l = f64(lse)
     assert np.isfinite(o).all(), f"{what}: non-finite output"
     diff = np.abs(o - ref_out)
-    err = diff.max()
-    excess = (diff - half_ulp(ref_out, dtype)).max()
-    rel = err / max(np.abs(ref_out).max(), 1e-30)
-    lerr = np.abs(l - ref_lse).max()
-    say(f"  {what}: max|err| {err:.3e}  beyond-rounding {excess:.3e}  rel {rel:.3e}  "
-        f"lse err {lerr:.3e}")
-    assert excess <= TOL[dtype], f"{what}: error beyond output rounding {excess} > {TOL[dtype]}"
+    err = float(diff.max()) if diff.size else 0.0
+    excess = float((diff - half_ulp(ref_out, dtype)).max()) if diff.size else 0.0
+    omax = float(np.abs(ref_out).max()) if diff.size else 0.0
+    rel = err / max(omax, 1e-30)
+    lerr = float(np.abs(f64(lse) - ref_lse).max()) if lse is not None and diff.size else 0.0
+    say(f"  {what}: max|err| {err:.3e} (bound {TOL[dtype]:.0e})  beyond-rounding {excess:.3e}  "
+        f"max|O| {omax:.3e}  rel {rel:.3e}  lse err {lerr:.3e}")
+    record("attention", what, max_err=err, bound=TOL[dtype], beyond_rounding=excess,
+           max_abs_ref=omax, rel_err=rel, lse_err=lerr, lse_bound=LSE_TOL[dtype],
+           dtype=str(dtype).replace("torch.", ""))
+    assert err <= TOL[dtype], f"{what}: max|err| {err} > {TOL[dtype]}"
     assert rel <= REL_GUARD[dtype], f"{what}: error {rel} of max |O|"
     assert lerr <= LSE_TOL[dtype], f"{what}: lse error {lerr}"
     return err

@@ -1,8 +1,7 @@
 """GPU parity of orthrus_block_attn against the fp64 oracle (through the C ABI).
 
-Covers the five workloads (full size where the oracle is fast, sampled
-requests / KV heads at full size otherwise, in the launch configuration the
-benchmark uses), edge cases (empty prefix, ragged tails, K=1 and K=64, D=64,
+Covers the five workloads at full size, every request and every head, in the
+launch configuration the benchmark uses, edge cases (empty prefix, ragged tails, K=1 and K=64, D=64,
 G=1 and G=16, ragged contiguous batches, a wrong max_len hint), and GPU
 metamorphic properties (split-count invariance, paged == contiguous,
 run-to-run determinism, causal last row == bidirectional last row).
@@ -55,14 +54,12 @@ def config4_step():
 
 
 @pytest.mark.parametrize("view", VIEWS)
-def test_config4_paged_sampled_requests(view, config4_step):
+def test_config4_paged_all_requests(view, config4_step):
     step = config4_step
     say(f"config4 paged view={view} lens={step.lens.tolist()[:8]}...")
     out, lse = gpu_attn(step, step.layers[0], view, max_len=8192)
-    lens = step.lens.tolist()
-    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 13, 31})
-    ro, rl = oracle_attn(step, step.layers[0], view, requests=sample)
-    assert_attn_close(out[sample], lse[sample], ro, rl, torch.bfloat16, f"config4 req {sample}")
+    ro, rl = oracle_attn(step, step.layers[0], view)
+    assert_attn_close(out, lse, ro, rl, torch.bfloat16, f"config4 all 32 requests {view}")
 
 
 @pytest.fixture(scope="module")
@@ -91,10 +88,9 @@ def test_config5_long_context_64_splits(K, view, long_cache):
     step = W.StepInputs(cfg, lens, None, 0, L_cap := kc.shape[2], [lay], None, None)
     say(f"config5 K={K} view={view}")
     out, lse = gpu_attn(step, lay, view, num_splits=64, max_len=131072)
-    g = K % 8
-    ro, rl = oracle_attn(step, lay, view, kv_heads=[g])
-    hs = list(range(4 * g, 4 * g + 4))
-    assert_attn_close(out[:, :, hs], lse[:, hs], ro, rl, torch.bfloat16, f"config5 K={K} head {g}")
+    # every KV head (all 32 query heads), against the whole 131,072-key cache
+    ro, rl = oracle_attn(step, lay, view)
+    assert_attn_close(out, lse, ro, rl, torch.bfloat16, f"config5 K={K} {view} all heads")
     assert L_cap == 131136
 
 
@@ -152,16 +148,49 @@ def test_forced_splits_and_wrong_hint():
 
 
 def test_split_count_invariance_and_determinism():
+    """Results for 1, 2, 8 and 32 splits agree with each other and with the
+    oracle, and each is bit-identical from run to run.
+
+    Two split plans differ by the rounding of the split partials (bf16, half
+    an ulp: |O_s| * 2^-9, with |O_s| <= max |V| since a partial is a convex
+    combination of V rows) and by the final output rounding (half an ulp of
+    |O| each), so |O_a - O_b| <= 2^-9 max|V| + 2^-8 max|O| (+ fp32 terms)."""
     step = W.custom_step(1, 32, 8, 128, 32, [4096], seed=11)
+    lay = step.layers[0]
+    ro, rl = oracle_attn(step, lay, "ar")
+    vmax = max(float(lay.v_cache.float().abs().max()), float(lay.v_blk_ar.float().abs().max()))
+    bound = 2.0 ** -9 * vmax + 2.0 ** -8 * float(np.abs(ro).max()) + 1e-5
     outs = []
     for ns in (1, 2, 8, 32):
-        o, l = gpu_attn(step, step.layers[0], "ar", num_splits=ns)
-        o2, l2 = gpu_attn(step, step.layers[0], "ar", num_splits=ns)
+        o, l = gpu_attn(step, lay, "ar", num_splits=ns)
+        o2, l2 = gpu_attn(step, lay, "ar", num_splits=ns)
         assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "not deterministic"
         assert torch.equal(l, l2)
+        assert_attn_close(o, l, ro, rl, torch.bfloat16, f"split invariance splits={ns}")
         outs.append(f64(o))
-    for o in outs[1:]:
-        assert np.abs(o - outs[0]).max() <= 4e-3
+    for ns, o in zip((2, 8, 32), outs[1:]):
+        d = float(np.abs(o - outs[0]).max())
+        say(f"  splits={ns} vs 1: max diff {d:.3e} (bound {bound:.3e})")
+        assert d <= bound
+
+
+def test_bf16_partials_error_budget():
+    """The split partials are stored in bf16: their rounding adds at most
+    2^-9 max|V| to the error.  Measured at the Qwen3-8B layer shape (8,192
+    keys, 26 splits) against the single-split launch of the same inputs."""
+    step = W.step_inputs(W.CONFIGS[3], layers=1, with_logits=False)
+    lay = step.layers[0]
+    for view in VIEWS:
+        ro, rl = oracle_attn(step, lay, view)
+        o1, l1 = gpu_attn(step, lay, view, num_splits=1, max_len=8192)
+        oa, la = gpu_attn(step, lay, view, max_len=8192)
+        e1 = assert_attn_close(o1, l1, ro, rl, torch.bfloat16, f"config3 {view} one split")
+        ea = assert_attn_close(oa, la, ro, rl, torch.bfloat16, f"config3 {view} auto splits")
+        vmax = max(float(lay.v_cache.float().abs().max()),
+                   float(getattr(lay, f"v_blk_{view}").float().abs().max()))
+        say(f"  config3 {view}: bf16 partials add {ea - e1:+.3e} to max|err| "
+            f"(budget {2.0 ** -9 * vmax:.3e})")
+        assert ea - e1 <= 2.0 ** -9 * vmax
 
 
 def test_paged_equals_contiguous_bitwise():

@@ -57,6 +57,9 @@ SIGNATURES = {
     "orthrus_block_attn": (_I, [_CP, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                                 _P, _SZ, _P]),
     "orthrus_block_attn_workspace_bytes": (_SZ, [_CP, _I, _I, _I, _I, _I, _I, _I]),
+    "orthrus_mdiff_attn": (_I, [_P, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                _I, _I, _F, _I, _P, _SZ, _P]),
+    "orthrus_mdiff_attn_workspace_bytes": (_SZ, [_I64, _I64, _I, _I, _I, _I, _I, _I, _I, _I]),
     "orthrus_consensus": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "orthrus_consensus_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "orthrus_argmax": (_I, [_P, _I64, _I, _I, _P, _P, _SZ, _P]),
@@ -64,6 +67,7 @@ SIGNATURES = {
     "orthrus_lmhead_argmax": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "orthrus_lmhead_argmax_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "orthrus_kv_append": (_I, [_CP, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I64, _P]),
+    "orthrus_stream_read": (_I, [_P, _SZ, _I, _P, _P]),
     "orthrus_status_string": (ctypes.c_char_p, [_I]),
     "orthrus_version": (_I, []),
 }
@@ -156,6 +160,22 @@ def orthrus_block_attn_workspace_bytes(cache, B, K, Hq, Hkv, D, dtype, num_split
                                                     num_splits)
 
 
+def orthrus_mdiff_attn(k_ctx, v_ctx, ctx_capacity, anchors, max_anchor, q, k_blk, v_blk, out,
+                       lse, B, NB, K, Hq, Hkv, D, dtype, scale, num_splits, workspace,
+                       workspace_bytes, stream=None) -> int:
+    return lib().orthrus_mdiff_attn(ptr(k_ctx), ptr(v_ctx), ctx_capacity, ptr(anchors),
+                                    max_anchor, ptr(q), ptr(k_blk), ptr(v_blk), ptr(out), ptr(lse),
+                                    B, NB, K, Hq, Hkv, D, dtype, scale, num_splits, ptr(workspace),
+                                    workspace_bytes,
+                                    stream if isinstance(stream, int) else stream_handle(stream))
+
+
+def orthrus_mdiff_attn_workspace_bytes(ctx_capacity, max_anchor, B, NB, K, Hq, Hkv, D, dtype,
+                                       num_splits) -> int:
+    return lib().orthrus_mdiff_attn_workspace_bytes(ctx_capacity, max_anchor, B, NB, K, Hq, Hkv,
+                                                    D, dtype, num_splits)
+
+
 def orthrus_consensus(diff_logits, ar_logits, B, K, V, dtype, diff_tok, ar_tok, n_match, n_emit,
                       emit_off, emitted, next_anchor, workspace, workspace_bytes,
                       stream=None) -> int:
@@ -196,6 +216,11 @@ def orthrus_kv_append(cache, k_blk, v_blk, n_emit, lens_out, B, K, Hkv, D, dtype
                                    ptr(lens_out), B, K, Hkv, D, dtype, num_layers,
                                    cache_layer_stride, blk_layer_stride,
                                    stream if isinstance(stream, int) else stream_handle(stream))
+
+
+def orthrus_stream_read(src, nbytes, work_groups, sink, stream=None) -> int:
+    return lib().orthrus_stream_read(ptr(src), nbytes, work_groups, ptr(sink),
+                                     stream if isinstance(stream, int) else stream_handle(stream))
 
 
 def orthrus_status_string(status: int) -> str:

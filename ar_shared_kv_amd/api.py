@@ -17,7 +17,33 @@ def dtype_code(t: torch.Tensor) -> int:
         raise TypeError(f"unsupported dtype {t.dtype}") from None
 
 
+def _need(name, t, *, dtype=None, shape=None, device=None):
+    """Host-side checks before a device pointer crosses the C ABI: the library
+    reads dense row-major buffers, so a view with other strides, another
+    element type or another device would be read as garbage."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous (call .contiguous())")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    return t
+
+
 def make_cache(k, v, lens, *, page_table=None, max_len=0):
+    _need("k_cache", k)
+    _need("v_cache", v, dtype=k.dtype, shape=k.shape, device=k.device)
+    if k.dim() != 4:
+        raise ValueError("cache tensors are [B, Hkv, cap, D] or [pages, Hkv, page, D]")
+    _need("lens", lens, dtype=torch.int32, device=k.device)
+    if page_table is not None:
+        _need("page_table", page_table, dtype=torch.int32, device=k.device)
+        if page_table.dim() != 2 or page_table.shape[0] != lens.shape[0]:
+            raise ValueError("page_table must be [B, max_pages] with B = len(lens)")
     return B_.make_cache(k, v, lens, page_table=page_table, max_len=max_len)
 
 
@@ -31,14 +57,28 @@ def block_attn_workspace(cache, B, K, Hq, Hkv, D, dtype, num_splits=0, device=No
 def block_attn(q, k_blk, v_blk, cache, *, mask, scale=None, num_splits=0, out=None, lse=None,
                want_lse=True, workspace=None, stream=None):
     """Shared-KV block attention of one layer; returns (out, lse)."""
+    if q.dim() != 4 or k_blk.dim() != 4:
+        raise ValueError("q is [B, K, Hq, D] and k_blk/v_blk [B, K, Hkv, D]")
     Bn, K, Hq, D = q.shape
     Hkv = k_blk.shape[2]
     dt = dtype_code(q)
+    _need("q", q)
+    _need("k_blk", k_blk, dtype=q.dtype, shape=(Bn, K, Hkv, D), device=q.device)
+    _need("v_blk", v_blk, dtype=q.dtype, shape=(Bn, K, Hkv, D), device=q.device)
+    ck = cache._keep[0]
+    if ck.dtype != q.dtype or ck.device != q.device or ck.shape[1] != Hkv or ck.shape[3] != D:
+        raise ValueError(f"cache {tuple(ck.shape)} {ck.dtype} does not match q/k_blk "
+                         f"(Hkv={Hkv}, D={D}, {q.dtype})")
+    if cache._keep[2].shape[0] != Bn:
+        raise ValueError("cache lens has another batch size than q")
     scale = D ** -0.5 if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
+    _need("out", out, dtype=q.dtype, shape=q.shape, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((Bn, Hq, K), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need("lse", lse, dtype=torch.float32, shape=(Bn, Hq, K), device=q.device)
     if workspace is None:
         workspace, nbytes = block_attn_workspace(cache, Bn, K, Hq, Hkv, D, dt, num_splits, q.device)
     else:
@@ -46,6 +86,43 @@ def block_attn(q, k_blk, v_blk, cache, *, mask, scale=None, num_splits=0, out=No
     st = B_.orthrus_block_attn(cache, q, k_blk, v_blk, out, lse, Bn, K, Hq, Hkv, D, dt, mask,
                                scale, num_splits, workspace, nbytes, stream)
     B_.check("orthrus_block_attn", st)
+    return out, lse
+
+
+def mdiff_attn(q, k_blk, v_blk, k_ctx, v_ctx, anchors, *, scale=None, max_anchor=0,
+               num_splits=0, out=None, lse=None, want_lse=True, workspace=None, stream=None):
+    """Training-time block-mask (M_diff) attention, forward: q [B, NB, K, Hq, D],
+    k_blk/v_blk [B, NB, K, Hkv, D], k_ctx/v_ctx [B, Hkv, cap, D], anchors
+    int32 [B, NB].  Returns (out, lse)."""
+    if q.dim() != 5 or k_blk.dim() != 5 or k_ctx.dim() != 4:
+        raise ValueError("q/k_blk/v_blk are [B, NB, K, H, D] and k_ctx/v_ctx [B, Hkv, cap, D]")
+    Bn, NB, K, Hq, D = q.shape
+    Hkv = k_blk.shape[3]
+    cap = k_ctx.shape[2]
+    dt = dtype_code(q)
+    _need("q", q)
+    for name, t in (("k_blk", k_blk), ("v_blk", v_blk)):
+        _need(name, t, dtype=q.dtype, shape=(Bn, NB, K, Hkv, D), device=q.device)
+    for name, t in (("k_ctx", k_ctx), ("v_ctx", v_ctx)):
+        _need(name, t, dtype=q.dtype, shape=(Bn, Hkv, cap, D), device=q.device)
+    _need("anchors", anchors, dtype=torch.int32, shape=(Bn, NB), device=q.device)
+    scale = D ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _need("out", out, dtype=q.dtype, shape=q.shape, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((Bn, NB, Hq, K), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need("lse", lse, dtype=torch.float32, shape=(Bn, NB, Hq, K), device=q.device)
+    n = B_.orthrus_mdiff_attn_workspace_bytes(cap, max_anchor, Bn, NB, K, Hq, Hkv, D, dt,
+                                              num_splits)
+    if workspace is None:
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = B_.orthrus_mdiff_attn(k_ctx, v_ctx, cap, anchors, max_anchor, q, k_blk, v_blk, out, lse,
+                               Bn, NB, K, Hq, Hkv, D, dt, scale, num_splits, workspace, nbytes,
+                               stream)
+    B_.check("orthrus_mdiff_attn", st)
     return out, lse
 
 
@@ -75,6 +152,11 @@ class ConsensusBuffers:
 def consensus(diff_logits, ar_logits, bufs: ConsensusBuffers | None = None, stream=None):
     Bn, K, V = ar_logits.shape
     dt = dtype_code(ar_logits)
+    _need("ar_logits", ar_logits)
+    _need("diff_logits", diff_logits, dtype=ar_logits.dtype, shape=ar_logits.shape,
+          device=ar_logits.device)
+    if bufs is not None and (bufs.B, bufs.K, bufs.V, bufs.dtype) != (Bn, K, V, dt):
+        raise ValueError("ConsensusBuffers were made for another (B, K, V, dtype)")
     if bufs is None:
         bufs = ConsensusBuffers(Bn, K, V, dt, ar_logits.device)
     st = B_.orthrus_consensus(diff_logits, ar_logits, Bn, K, V, dt, bufs.diff_tok, bufs.ar_tok,
@@ -88,6 +170,7 @@ def argmax(logits, stream=None):
     V = logits.shape[-1]
     rows = logits.numel() // V
     dt = dtype_code(logits)
+    _need("logits", logits)
     idx = torch.empty(rows, dtype=torch.int32, device=logits.device)
     n = B_.orthrus_argmax_workspace_bytes(rows, V, dt)
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=logits.device)
@@ -102,8 +185,15 @@ def lmhead_argmax(hidden, weight, idx=None, workspace=None, stream=None):
     R = hidden.numel() // H
     V = weight.shape[0]
     dt = dtype_code(hidden)
+    _need("hidden", hidden)
+    if weight.dim() != 2:
+        raise ValueError("weight is [V, H]")
+    _need("weight", weight, dtype=hidden.dtype, shape=(V, H), device=hidden.device)
     if idx is None:
         idx = torch.empty(R, dtype=torch.int32, device=hidden.device)
+    _need("idx", idx, dtype=torch.int32, device=hidden.device)
+    if idx.numel() != R:
+        raise ValueError(f"idx holds {idx.numel()} entries for {R} rows")
     n = B_.orthrus_lmhead_argmax_workspace_bytes(R, H, V, dt)
     if workspace is None:
         workspace = torch.empty(max(n, 8), dtype=torch.uint8, device=hidden.device)
@@ -117,8 +207,16 @@ def kv_append(cache, k_blk, v_blk, n_emit, lens_out=None, *, num_layers=1,
               cache_layer_stride=0, blk_layer_stride=0, stream=None):
     """Append accepted AR rows; k_blk/v_blk are layer 0's [B, K, Hkv, D]."""
     Bn, K, Hkv, D = k_blk.shape[-4:]
+    _need("k_blk", k_blk)
+    _need("v_blk", v_blk, dtype=k_blk.dtype, shape=k_blk.shape, device=k_blk.device)
+    _need("n_emit", n_emit, dtype=torch.int32, shape=(Bn,), device=k_blk.device)
+    ck = cache._keep[0]
+    if ck.dtype != k_blk.dtype or ck.device != k_blk.device or ck.shape[1] != Hkv \
+            or ck.shape[3] != D:
+        raise ValueError("cache and block rows differ in dtype, device, Hkv or D")
     if lens_out is None:
         lens_out = torch.empty(Bn, dtype=torch.int32, device=k_blk.device)
+    _need("lens_out", lens_out, dtype=torch.int32, shape=(Bn,), device=k_blk.device)
     st = B_.orthrus_kv_append(cache, k_blk, v_blk, n_emit, lens_out, Bn, K, Hkv, D,
                               dtype_code(k_blk), num_layers, cache_layer_stride, blk_layer_stride,
                               stream)

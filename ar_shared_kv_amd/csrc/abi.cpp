@@ -150,10 +150,17 @@ size_t orthrus_block_attn_workspace_bytes(const orthrus_cache *cache, int B, int
     return pl.status == ORTHRUS_OK ? pl.ws_bytes : 0;
 }
 
-int orthrus_block_attn(const orthrus_cache *cache, const void *q, const void *k_blk,
-                       const void *v_blk, void *out, float *lse, int B, int K, int Hq, int Hkv,
-                       int D, int dtype, int mask, float scale, int num_splits, void *workspace,
-                       size_t workspace_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// The block attention launch shared by the decode step (nbps = 1: request b
+// reads its own cache) and the training-time block mask (nbps = blocks per
+// sequence: block b reads the context of sequence b / nbps).
+int block_attn_impl(const orthrus_cache *cache, const void *q, const void *k_blk,
+                    const void *v_blk, void *out, float *lse, int B, int K, int Hq, int Hkv,
+                    int D, int dtype, int mask, float scale, int num_splits, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream, int nbps, int reverse)
 {
     if (!cache || !q || !k_blk || !v_blk || !out) return ORTHRUS_ERR_NULL;
     if (!cache->k || !cache->v || !cache->lens) return ORTHRUS_ERR_NULL;
@@ -197,11 +204,72 @@ int orthrus_block_attn(const orthrus_cache *cache, const void *q, const void *k_
     p.c = scale * 1.4426950408889634f;
     p.lpt = (cache->layout == ORTHRUS_LAYOUT_PAGED && dtype == ORTHRUS_BF16 && B <= 64 &&
              pl.S_grid > 1) ? 1 : 0;
+    p.nbps = nbps;
+    p.reverse = reverse;
     if (pl.S_grid > 1) {
         p.ws_o = workspace;
         p.ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.ws_lse_offset);
     }
     return map_err(launch_block_attn(p, dtype, stream));
+}
+
+// The context of a training-time block-mask call as a contiguous cache of
+// B*NB requests (the anchors are the lengths).
+bool mdiff_cache(orthrus_cache *c, const void *k_ctx, const void *v_ctx, int64_t ctx_capacity,
+                 const int32_t *anchors, int64_t max_anchor, int B, int NB)
+{
+    if (B < 1 || NB < 1 || ctx_capacity < 0 || max_anchor < 0 || max_anchor > ctx_capacity ||
+        (int64_t)B * NB > (int64_t)1 << 24)
+        return false;
+    *c = orthrus_cache{};
+    c->layout = ORTHRUS_LAYOUT_CONTIGUOUS;
+    c->page_size = 16;
+    c->k = const_cast<void *>(k_ctx);
+    c->v = const_cast<void *>(v_ctx);
+    c->capacity = ctx_capacity;
+    c->lens = anchors;
+    c->max_len = max_anchor;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int orthrus_block_attn(const orthrus_cache *cache, const void *q, const void *k_blk,
+                       const void *v_blk, void *out, float *lse, int B, int K, int Hq, int Hkv,
+                       int D, int dtype, int mask, float scale, int num_splits, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream)
+{
+    return block_attn_impl(cache, q, k_blk, v_blk, out, lse, B, K, Hq, Hkv, D, dtype, mask, scale,
+                           num_splits, workspace, workspace_bytes, stream, 1, 0);
+}
+
+size_t orthrus_mdiff_attn_workspace_bytes(int64_t ctx_capacity, int64_t max_anchor, int B, int NB,
+                                          int K, int Hq, int Hkv, int D, int dtype,
+                                          int num_splits)
+{
+    orthrus_cache c;
+    if (!mdiff_cache(&c, nullptr, nullptr, ctx_capacity, nullptr, max_anchor, B, NB)) return 0;
+    AttnPlan pl = plan_block_attn(&c, B * NB, K, Hq, Hkv, D, dtype, num_splits);
+    return pl.status == ORTHRUS_OK ? pl.ws_bytes : 0;
+}
+
+int orthrus_mdiff_attn(const void *k_ctx, const void *v_ctx, int64_t ctx_capacity,
+                       const int32_t *anchors, int64_t max_anchor, const void *q,
+                       const void *k_blk, const void *v_blk, void *out, float *lse, int B, int NB,
+                       int K, int Hq, int Hkv, int D, int dtype, float scale, int num_splits,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!k_ctx || !v_ctx || !anchors) return ORTHRUS_ERR_NULL;
+    orthrus_cache c;
+    if (!mdiff_cache(&c, k_ctx, v_ctx, ctx_capacity, anchors, max_anchor, B, NB))
+        return ORTHRUS_ERR_SHAPE;
+    // blocks are dispatched from the last one: with anchors growing along the
+    // sequence that is longest first, so the long blocks do not start last
+    return block_attn_impl(&c, q, k_blk, v_blk, out, lse, B * NB, K, Hq, Hkv, D, dtype,
+                           ORTHRUS_MASK_BIDIR, scale, num_splits, workspace, workspace_bytes,
+                           stream, NB, 1);
 }
 
 size_t orthrus_consensus_workspace_bytes(int B, int K, int V, int dtype)
@@ -276,7 +344,6 @@ int orthrus_kv_append(const orthrus_cache *cache, const void *k_blk, const void 
     if (B < 1 || K < 1 || Hkv < 1 || D < 1 || num_layers < 1 || cache_layer_stride < 0 ||
         blk_layer_stride < 0)
         return ORTHRUS_ERR_SHAPE;
-    if (lens_out == cache->lens) return ORTHRUS_ERR_SHAPE;
     if (K > 64 || (D != 64 && D != 128) || B > 8192) return ORTHRUS_ERR_UNSUPPORTED;
     const int esize = dtype == ORTHRUS_BF16 ? 2 : 4;
     if (cache->layout == ORTHRUS_LAYOUT_CONTIGUOUS) {
@@ -310,6 +377,7 @@ int orthrus_kv_append(const orthrus_cache *cache, const void *k_blk, const void 
     p.maxp = cache->max_pages_per_req;
     p.cache_layer_stride = cache_layer_stride;
     p.blk_layer_stride = blk_layer_stride;
+    p.lens_in_place = lens_out == cache->lens ? 1 : 0;
     return map_err(launch_kv_append(p, stream));
 }
 

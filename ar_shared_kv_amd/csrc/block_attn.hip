@@ -176,6 +176,7 @@ attn_bf16_kernel(AttnParams p)
     const int BH = p.B * p.Hkv;
     int bh = blockIdx.x % BH;
     int s = blockIdx.x / BH;
+    if (!PAGED && p.reverse) bh = BH - 1 - bh;
     if (PAGED && p.lpt) {             // longest-first work list
         int bi, si;
         if (!lpt_item(p, blockIdx.x / p.Hkv, lane, bi, si)) return;
@@ -230,7 +231,7 @@ attn_bf16_kernel(AttnParams p)
     // reads; V rows by 2*(row & 3) for the transposed 8-byte reads.
     const char* kc = (const char*)p.kc;
     const char* vc = (const char*)p.vc;
-    const int64_t cont_base = ((int64_t)b * p.Hkv + g) * p.cap * D * 2;    // bytes
+    const int64_t cont_base = ((int64_t)(b / p.nbps) * p.Hkv + g) * p.cap * D * 2;    // bytes
     const int64_t blk_base = ((int64_t)b * p.K * p.Hkv + g) * D * 2;
     const int blk_stride = p.Hkv * D * 2;
     // Load i of a tile by this lane (K chunks first, then V): the tile row it
@@ -702,7 +703,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams p)
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int BH = p.B * p.Hkv;
-    const int bh = blockIdx.x % BH;
+    const int bh = p.reverse ? BH - 1 - (int)(blockIdx.x % BH) : (int)(blockIdx.x % BH);
     const int s = blockIdx.x / BH;
     const int b = bh / p.Hkv;
     const int g = bh % p.Hkv;
@@ -762,7 +763,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnParams p)
                 } else {
                     const int key = start + row;
                     if (p.layout == 0) {
-                        off = (((int64_t)b * p.Hkv + g) * p.cap + key) * D + d;
+                        off = (((int64_t)(b / p.nbps) * p.Hkv + g) * p.cap + key) * D + d;
                     } else {
                         const int page = p.page_table[(int64_t)b * p.maxp + (key >> 4)];
                         off = (((int64_t)page * p.Hkv + g) * 16 + (key & 15)) * D + d;

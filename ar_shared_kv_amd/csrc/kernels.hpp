@@ -32,6 +32,10 @@ struct AttnParams {
     float c;                          // scale * log2(e)
     int lpt;                          // paged, B <= 64: blockIdx.x walks a longest-first
                                       // list of (request, split) work items
+    int nbps;                         // requests per cache sequence: request b reads the
+                                      // contiguous cache of sequence b / nbps (1 = its own)
+    int reverse;                      // dispatch requests from the last one (longest first
+                                      // when lengths grow with the request index)
 };
 
 int attn_rows_per_wg(int dtype, int M);
@@ -57,6 +61,7 @@ struct AppendParams {
     int32_t *lens_out;
     int B, K, Hkv, D, esize, layers, layout;
     int64_t cap, maxp, cache_layer_stride, blk_layer_stride;   // elements
+    int lens_in_place;                // lens_out == lens: a second launch advances lens
 };
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t st);
 

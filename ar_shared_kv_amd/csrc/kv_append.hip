@@ -54,7 +54,7 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendParams p, int chun
     }
     if (tid == 255) off[p.B] = part[255];
     __syncthreads();
-    if (layer == 0 && chunk == 0) {
+    if (layer == 0 && chunk == 0 && !p.lens_in_place) {
         for (int b = tid; b < p.B; b += 256) p.lens_out[b] = p.lens[b] + (off[b + 1] - off[b]);
     }
 
@@ -99,11 +99,32 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendParams p, int chun
     }
 }
 
+// lens_out = lens + n, one thread per request: the second launch of an
+// in-place append (lens_out aliases lens), which must follow every read of
+// lens by the copy launch.
+__global__ void __launch_bounds__(256) lens_advance_kernel(const int32_t *lens,
+                                                           const int32_t *n_emit, int32_t *lens_out,
+                                                           int B, int K)
+{
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b >= B) return;
+    int n = n_emit[b];
+    n = n < 0 ? 0 : (n > K ? K : n);
+    lens_out[b] = lens[b] + n;
+}
+
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t st)
 {
     const int chunks = (p.B * p.K + kAppendRowsPerWG - 1) / kAppendRowsPerWG;
     hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)(chunks * p.layers)), dim3(256), 0, st, p,
                        chunks);
+    if (!p.lens_in_place) return hipGetLastError();
+    // every work-group of the copy reads lens[b] to place its rows, so an
+    // update in place waits for the whole copy: stream order does that
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lens_advance_kernel, dim3((unsigned)((p.B + 255) / 256)), dim3(256), 0, st,
+                       p.lens, p.n_emit, p.lens_out, p.B, p.K);
     return hipGetLastError();
 }
 

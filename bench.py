@@ -7,8 +7,16 @@ prefix L=8192, block K=32, vocabulary 151,936) is:
     consensus over both views' logits [1, 32, 151936]
     append of the accepted rows' KV on all 36 layers
 Every layer has its own synthetic cache (1.2 GB in total, resident in HBM).
-The step is captured in a HIP graph; W warm-up replays, then K timed replays
-between two synchronisations.  Prints ONE JSON line.
+Consecutive steps cycle 16 seeded draws of the consensus logits (match
+probability 0.85), so the accepted lengths vary from step to step; the JSON
+line reports their mean and histogram.  The steps are captured in a HIP
+graph; W warm-up replays, then 5 repeats of K timed replays, each between two
+synchronisations; the median repeat is reported.  Prints ONE JSON line.
+
+The block attention (the dominant kernel) is timed alone as well, and next to
+it the read-only streaming ceiling of one launch that reads the same number of
+bytes (orthrus_stream_read over distinct buffers back to back):
+"roofline.frac_of_ceiling".  --stream-ceiling prints only that ceiling.
 
 --config N runs another workload (1 tiny fp32, 2 Qwen3-1.7B layer, 4 paged
 serving, 5 long context with --K in {4, 8, 16, 32, 64}).  A workload whose
@@ -69,7 +77,7 @@ def measured_traffic(workload, splits, name=None, sources=ATTN_SOURCES):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, help="workload id (3 = the headline one)")
     ap.add_argument("--K", type=int, default=0, help="block size override (long-context sweep)")
@@ -87,6 +95,19 @@ def parse():
     ap.add_argument("--calib-bytes", type=int, default=0,
                     help="first run one plain device copy of this many bytes (a known-size "
                          "kernel for scaling hardware byte counters)")
+    ap.add_argument("--draws", type=int, default=0,
+                    help="seeded consensus-logits draws cycled by consecutive steps "
+                         "(0 = 16 when they fit in 512 MiB, else 1)")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed repeats of --steps replays; the median is reported")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="only measure the read-only streaming ceiling of one launch "
+                         "(34 MB and 537 MB per launch, distinct buffers back to back)")
+    ap.add_argument("--mdiff", action="store_true",
+                    help="time the training-time block-mask (M_diff) attention forward on a "
+                         "4 x 4,096-token micro-batch at the Qwen3-8B shape instead")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-ceiling measurement of the default run")
     return ap.parse_args()
 
 
@@ -97,7 +118,7 @@ def log(*a):
 class Step:
     """Device-resident inputs and outputs of one decode step of a workload."""
 
-    def __init__(self, cfg, splits, sets=0, dev="cuda"):
+    def __init__(self, cfg, splits, sets=0, draws=0, dev="cuda"):
         import torch
         import workloads as W
         from ar_shared_kv_amd import api
@@ -147,9 +168,25 @@ class Step:
                 x[si * nl:(si + 1) * nl].copy_(x[:nl])
         log(f"inputs for {nl} layers x {sets} input sets generated in {time.time() - t0:.1f}s")
         self.step_inputs = st
-        dl, al = st.diff_logits.to(dev), st.ar_logits.to(dev)
-        self.diff_logits = [dl] + [dl.clone() for _ in range(1, sets)]
-        self.ar_logits = [al] + [al.clone() for _ in range(1, sets)]
+        # Consensus logits: `draws` independent seeded draws (the workload's
+        # match probabilities), cycled by consecutive steps so that the
+        # accepted lengths vary as they would over a generation.
+        lbytes = e * (st.diff_logits.numel() + st.ar_logits.numel())
+        if draws <= 0:
+            draws = 16 if 16 * lbytes <= (512 << 20) else 1
+        self.draws = draws
+        # steps per replay: every input set and every draw at least once
+        self.nsteps = max(sets, draws)
+        self.diff_logits, self.ar_logits = [], []
+        for d in range(draws):
+            if d == 0:
+                dl, al = st.diff_logits, st.ar_logits
+            else:
+                dl, al = W.consensus_logits(cfg.B, cfg.K, cfg.V, W.match_probabilities(cfg),
+                                            cfg.torch_dtype,
+                                            W.seed_of(cfg, W.T_LOGITS, salt=1000 + d))
+            self.diff_logits.append(dl.to(dev))
+            self.ar_logits.append(al.to(dev))
         lmax = int(st.lens.max())
         self.caches = [api.make_cache(self.kc[l], self.vc[l], self.lens,
                                       page_table=self.page_table, max_len=lmax)
@@ -159,7 +196,8 @@ class Step:
         dcode = api.dtype_code(self.q["ar"])
         self.ws, self.ws_bytes = api.block_attn_workspace(self.caches[0], cfg.B, cfg.K, cfg.Hq,
                                                           cfg.Hkv, cfg.D, dcode, splits, dev)
-        self.cbufs = api.ConsensusBuffers(cfg.B, cfg.K, cfg.V, dcode, dev)
+        self.cbufs = [api.ConsensusBuffers(cfg.B, cfg.K, cfg.V, dcode, dev)
+                      for _ in range(draws)]
 
     def attention(self, view, layer):
         from ar_shared_kv_amd import api
@@ -181,14 +219,16 @@ class Step:
             self.attention_set(si)
 
     def run(self):
-        """`sets` consecutive decode steps, one per input set."""
+        """`nsteps` consecutive decode steps: step j uses input set j % sets
+        and logits draw j % draws."""
         from ar_shared_kv_amd import api
         nl = self.cfg.layers
-        for si in range(self.sets):
+        for j in range(self.nsteps):
+            si, d = j % self.sets, j % self.draws
             self.attention_set(si)
-            api.consensus(self.diff_logits[si], self.ar_logits[si], self.cbufs)
+            bufs = api.consensus(self.diff_logits[d], self.ar_logits[d], self.cbufs[d])
             api.kv_append(self.caches[si * nl], self.kb["ar"][si * nl], self.vb["ar"][si * nl],
-                          self.cbufs.n_emit, self.lens_out, num_layers=nl,
+                          bufs.n_emit, self.lens_out, num_layers=nl,
                           cache_layer_stride=self.kc[0].numel(),
                           blk_layer_stride=self.kb["ar"][0].numel())
 
@@ -204,17 +244,24 @@ class Step:
         c = self.cfg
         return 4 * c.Hq * c.D * sum(c.K * (int(L) + c.K) for L in self.step_inputs.lens)
 
-    def step_bytes(self, n_total):
+    def step_bytes(self, n_mean_total):
+        """Algorithmic bytes of one step with n_mean_total accepted rows (summed
+        over the batch, averaged over the steps of a replay)."""
         c = self.cfg
         e = 2 if c.dtype == "bf16" else 4
         logits = 2 * c.B * c.K * c.V * e
-        append = 2 * 2 * c.Hkv * c.D * e * n_total * c.layers
+        append = 2 * 2 * c.Hkv * c.D * e * n_mean_total * c.layers
         return 2 * c.layers * self.attn_bytes_per_launch() + logits + append
 
 
-def timed(fn, steps, warmup, graph):
+def timed(fn, steps, warmup, graph, repeats=1, stream=None):
+    """Per-call milliseconds of `fn` (captured in a HIP graph unless graph is
+    False): warm-up calls, then `repeats` timed runs of `steps` calls, each
+    between two synchronisations and timed with events on the launch stream.
+    Returns (median ms, list of per-repeat ms)."""
+    import statistics
     import torch
-    s = torch.cuda.current_stream()
+    s = stream or torch.cuda.current_stream()
     if graph:
         g = torch.cuda.CUDAGraph()
         fn()
@@ -227,20 +274,60 @@ def timed(fn, steps, warmup, graph):
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(steps):
-        run()
-    e1.record(s)
+    per = []
+    for _ in range(max(1, repeats)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(steps):
+            run()
+        e1.record(s)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / steps)
+    return statistics.median(per), per
+
+
+def stream_ceiling(nbytes, n_buffers, wgs_list, steps=20, warmup=5):
+    """The read-only streaming rate of one launch reading `nbytes`, launches
+    back to back over `n_buffers` distinct buffers (so that the 256 MB
+    last-level cache cannot serve a repeat), captured in a HIP graph; one
+    entry per work-group count.  Every byte is read once per launch."""
+    import torch
+    from ar_shared_kv_amd import _binding as B_
+    nbytes -= nbytes % 16
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n_buffers)]
+    sink = torch.empty(max(wgs_list), dtype=torch.int32, device="cuda")
+    out = []
+    for wgs in wgs_list:
+        def launches(wgs=wgs):
+            for b in bufs:
+                B_.check("orthrus_stream_read", B_.orthrus_stream_read(b, nbytes, wgs, sink))
+        ms, _ = timed(launches, steps, warmup, True)
+        us = ms * 1e3 / n_buffers
+        out.append({"work_groups": wgs, "us_per_launch": round(us, 3),
+                    "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    del bufs
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, (g if graph else None)
+    return {"bytes_per_launch": nbytes, "buffers": n_buffers, "sweep": out,
+            "best_gbps": max(r["gbps"] for r in out)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(step: Step, budget_s: float):
-    """The oracle on the host cores: whole layers of the step until ~budget_s,
-    extrapolated to the full step (consensus and append timed once)."""
-    import numpy as np
+    """The oracle on the host cores: whole layers of the step until ~budget_s
+    with every thread, then one layer with one thread; each extrapolated to
+    the full step (consensus and a 1-layer append timed once per leg)."""
     import oracle
     import workloads as W
     cfg = step.cfg
@@ -250,40 +337,66 @@ def cpu_baseline(step: Step, budget_s: float):
     kw = dict(scale=cfg.scale)
     if cfg.paged:
         kw.update(layout=oracle.PAGED, page_table=pt)
-    t_layers = 0.0
-    done = 0
-    while done < cfg.layers:
-        lay = st.layers[0] if done == 0 else W.layer_inputs(cfg, done, st.lens, st.num_pages,
-                                                            st.capacity)
-        arrs = {k: getattr(lay, k).double().numpy() for k in
+    raw = lambda t: t.view(torch_int(t)).numpy()  # noqa: E731
+
+    def layer_arrays(l):
+        lay = st.layers[0] if l == 0 else W.layer_inputs(cfg, l, st.lens, st.num_pages,
+                                                        st.capacity)
+        return {k: getattr(lay, k).double().numpy() for k in
                 ("q_diff", "q_ar", "k_cache", "v_cache", "k_blk_diff", "v_blk_diff",
                  "k_blk_ar", "v_blk_ar")}
+
+    def layer_pair(a):
+        oracle.block_attn(a["q_diff"], a["k_cache"], a["v_cache"], a["k_blk_diff"],
+                          a["v_blk_diff"], lens, mask=oracle.BIDIR, **kw)
+        oracle.block_attn(a["q_ar"], a["k_cache"], a["v_cache"], a["k_blk_ar"],
+                          a["v_blk_ar"], lens, mask=oracle.CAUSAL, **kw)
+
+    def tail():
+        dl = st.diff_logits.double().numpy()
+        al = st.ar_logits.double().numpy()
         t0 = time.perf_counter()
-        oracle.block_attn(arrs["q_diff"], arrs["k_cache"], arrs["v_cache"], arrs["k_blk_diff"],
-                          arrs["v_blk_diff"], lens, mask=oracle.BIDIR, **kw)
-        oracle.block_attn(arrs["q_ar"], arrs["k_cache"], arrs["v_cache"], arrs["k_blk_ar"],
-                          arrs["v_blk_ar"], lens, mask=oracle.CAUSAL, **kw)
+        r = oracle.consensus(oracle.argmax_rows(dl), oracle.argmax_rows(al))
+        lay = st.layers[0]
+        t1 = time.perf_counter()
+        oracle.kv_append(raw(lay.k_cache)[None], raw(lay.v_cache)[None], raw(lay.k_blk_ar)[None],
+                         raw(lay.v_blk_ar)[None], r["n"], lens,
+                         layout=oracle.PAGED if cfg.paged else oracle.CONTIGUOUS, page_table=pt)
+        return t1 - t0, time.perf_counter() - t1
+
+    threads = oracle.num_threads()
+    t_layers, done = 0.0, 0
+    first = None
+    while done < cfg.layers:
+        a = layer_arrays(done)
+        if first is None:
+            first = a
+        t0 = time.perf_counter()
+        layer_pair(a)
         t_layers += time.perf_counter() - t0
         done += 1
         if t_layers >= budget_s:
             break
-    dl = st.diff_logits.double().numpy()
-    al = st.ar_logits.double().numpy()
-    t0 = time.perf_counter()
-    r = oracle.consensus(oracle.argmax_rows(dl), oracle.argmax_rows(al))
-    t_cons = time.perf_counter() - t0
-    raw = lambda t: t.view(torch_int(t)).numpy()  # noqa: E731
-    lay = st.layers[0]
-    t0 = time.perf_counter()
-    oracle.kv_append(raw(lay.k_cache)[None], raw(lay.v_cache)[None], raw(lay.k_blk_ar)[None],
-                     raw(lay.v_blk_ar)[None], r["n"], lens,
-                     layout=oracle.PAGED if cfg.paged else oracle.CONTIGUOUS, page_table=pt)
-    t_app = time.perf_counter() - t0
+    t_cons, t_app = tail()
     step_s = t_layers / done * cfg.layers + t_cons + t_app * cfg.layers
+    # one thread: a single layer pair (the cost per layer does not depend on
+    # which layer), consensus and the 1-layer append
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        layer_pair(first)
+        t1_layer = time.perf_counter() - t0
+        t1_cons, t1_app = tail()
+    finally:
+        oracle.set_num_threads(threads)
+    step1_s = t1_layer * cfg.layers + t1_cons + t1_app * cfg.layers
     sample = (f"oracle fp64 on {done} of {cfg.layers} layers (BIDIR+CAUSAL passes at full shape), "
-              f"consensus and a 1-layer append; extrapolated to the {cfg.layers}-layer step")
-    return {"value": round(1.0 / step_s, 6), "unit": "steps/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "sample": sample, "seconds_measured": round(t_layers + t_cons + t_app, 2)}
+              f"consensus and a 1-layer append, extrapolated to the {cfg.layers}-layer step; "
+              f"the 1-thread leg on 1 layer")
+    return {"value": round(1.0 / step_s, 6), "unit": "steps/s", "cores": threads,
+            "kind": "oracle", "sample": sample, "cpu_model": cpu_model(),
+            "value_1thread": round(1.0 / step1_s, 6),
+            "seconds_measured": round(t_layers + t_cons + t_app + t1_layer + t1_cons + t1_app, 2)}
 
 
 def torch_int(t):
@@ -321,7 +434,7 @@ def lmhead_main(args):
     n = B_.orthrus_lmhead_argmax_workspace_bytes(R, H, V, B_.BF16)
     ws = torch.empty(n, dtype=torch.uint8, device="cuda")
     call = lambda: api.lmhead_argmax(hd, wd, idx=idx, workspace=ws)
-    ms, _ = timed(call, args.steps, args.warmup, not args.no_graph)
+    ms, per = timed(call, args.steps, args.warmup, not args.no_graph, args.repeats)
     nbytes = V * H * 2 + R * H * 2 + R * 4
     gbps = nbytes / (ms * 1e-3) / 1e9
     flops = 2 * R * H * V
@@ -375,34 +488,46 @@ def main():
     if args.lmhead:
         lmhead_main(args)
         return
+    if args.stream_ceiling:
+        ceiling_main(args)
+        return
+    if args.mdiff:
+        mdiff_main(args)
+        return
     cfg = W.CONFIGS[args.config]
     if args.K:
         cfg = cfg.with_(K=args.K)
     splits = args.splits or cfg.num_splits
     log(f"workload {cfg.name} K={cfg.K} splits={splits or 'auto'}")
     calibrate(args.calib_bytes)
-    step = Step(cfg, splits, args.sets)
+    step = Step(cfg, splits, args.sets, args.draws)
     graph = not args.no_graph
 
-    ms_run, _ = timed(step.run, args.steps, args.warmup, graph)
-    ms_step = ms_run / step.sets
+    ms_run, per_run = timed(step.run, args.steps, args.warmup, graph, args.repeats)
+    ms_step = ms_run / step.nsteps
+    log(f"step: median {ms_step:.5f} ms over {args.repeats} repeats "
+        f"({', '.join(f'{m / step.nsteps:.5f}' for m in per_run)})")
     # the dominant kernel: block attention alone, all 2*layers passes per step
-    ms_attn_all, _ = timed(step.attention_passes, args.steps, args.warmup, graph)
+    ms_attn_all, per_attn = timed(step.attention_passes, args.steps, args.warmup, graph,
+                                  args.repeats)
     us_attn = ms_attn_all * 1e3 / (2 * cfg.layers * step.sets)
-    n = step.cbufs.n_emit.cpu()
-    n_total = int(n.sum())
+    # accepted rows of every draw (each draw's outputs are its own buffers)
+    import torch
+    n_all = torch.stack([b.n_emit for b in step.cbufs]).cpu()      # [draws, B]
+    n_mean_total = float(n_all.sum(dim=1).float().mean())
 
     attn_b = step.attn_bytes_per_launch()
     attn_f = step.attn_flops_per_launch()
     achieved_gbps = attn_b / (us_attn * 1e-6) / 1e9
     steps_s = 1e3 / ms_step
+    hist = torch.bincount(n_all.flatten().long(), minlength=cfg.K + 1).tolist()
     res = {
         "metric": METRIC,
         "value": round(steps_s, 3),
         "unit": "steps/s",
         "n_gpus": 1,
-        "steps": args.steps * step.sets,
-        "warmup": args.warmup * step.sets,
+        "steps": args.steps * step.nsteps,
+        "warmup": args.warmup * step.nsteps,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -412,18 +537,121 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
                    "K": cfg.K, "L": cfg.L if cfg.L_range is None else list(cfg.L_range),
                    "layers": cfg.layers, "V": cfg.V, "paged": cfg.paged,
-                   "num_splits": splits or "auto", "graph": graph, "input_sets": step.sets},
+                   "num_splits": splits or "auto", "graph": graph, "input_sets": step.sets,
+                   "logits_draws": step.draws},
+        "timing": {"repeats": args.repeats, "statistic": "median",
+                   "ms_per_step_repeats": [round(m / step.nsteps, 5) for m in per_run],
+                   "us_per_attn_launch_repeats":
+                       [round(m * 1e3 / (2 * cfg.layers * step.sets), 3) for m in per_attn]},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None if args.K else measured_traffic(cfg.name, args.splits),
                      "kernel": "block attention (attn_bf16_kernel + split merge), per launch",
                      "us_per_launch": round(us_attn, 3), "bytes_per_launch": attn_b,
                      "mfma_frac": round(attn_f / (us_attn * 1e-6) / 2.5e15, 4)},
-        "step_hbm_tbps": round(step.step_bytes(n_total) / (ms_step * 1e-3) / 1e12, 3),
-        "accepted_per_step": n.tolist() if cfg.B <= 4 else round(float(n.float().mean()), 3),
+        "step_hbm_tbps": round(step.step_bytes(n_mean_total) / (ms_step * 1e-3) / 1e12, 3),
+        "accepted": {"mean_n_per_request": round(n_mean_total / cfg.B, 3),
+                     "histogram_n": {str(i): c for i, c in enumerate(hist) if c},
+                     "samples": int(n_all.numel()),
+                     "expected_n": round(expected_n(cfg), 3)},
     }
+    if not args.no_ceiling:
+        # the same bytes per launch as one attention pass, read with nothing
+        # else to do, over enough distinct buffers to span 1 GiB
+        nbuf = max(4, -(-(1 << 30) // attn_b))
+        ceil = stream_ceiling(attn_b, nbuf, [208, 256, 512, 1024, 2048])
+        res["roofline"]["ceiling_gbps"] = ceil["best_gbps"]
+        res["roofline"]["frac_of_ceiling"] = round(achieved_gbps / ceil["best_gbps"], 4)
+        res["stream_ceiling"] = ceil
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def expected_n(cfg):
+    """E[n] = (1 - p^K) / (1 - p) per request, averaged over the batch's p."""
+    import workloads as W
+    p = W.match_probabilities(cfg)
+    ps = p if isinstance(p, (list, tuple)) else [p]
+    return sum(cfg.K if q >= 1 else (1 - q ** cfg.K) / (1 - q) for q in ps) / len(ps)
+
+
+def mdiff_main(args):
+    """The training-time block mask M_diff, forward: every block of K = 32
+    positions of 4 sequences of 4,096 tokens (Qwen3-8B attention shape) sees
+    the clean context before its anchor and its own block.  Bound: the matrix
+    cores (the FLOPs at peak take longer than the unique bytes at peak)."""
+    import torch
+    import workloads as W
+    from ar_shared_kv_amd import api
+    wl = W.MDIFF_WORKLOAD
+    Bn, N, K, Hq, Hkv, D = wl["B"], wl["N"], wl["K"], wl["Hq"], wl["Hkv"], wl["D"]
+    inp = W.mdiff_inputs(Bn, N, K, Hq, Hkv, D, layout=wl["layout"])
+    d = {k: getattr(inp, k).cuda() for k in ("q", "k_blk", "v_blk", "k_ctx", "v_ctx", "anchors")}
+    out = torch.empty_like(d["q"])
+    NB = inp.q.shape[1]
+    lse = torch.empty((Bn, NB, Hq, K), dtype=torch.float32, device="cuda")
+    call = lambda: api.mdiff_attn(d["q"], d["k_blk"], d["v_blk"], d["k_ctx"], d["v_ctx"],  # noqa
+                                  d["anchors"], max_anchor=N, out=out, lse=lse)
+    ms, per = timed(call, args.steps, args.warmup, not args.no_graph, args.repeats)
+    a = inp.anchors.long()
+    flops = 4 * Hq * D * K * int((a + K).sum())
+    e = 2
+    nbytes = (2 * Bn * Hkv * N * D * e + 2 * inp.q.numel() * e + 2 * inp.k_blk.numel() * e
+              + 4 * lse.numel())
+    tf = flops / (ms * 1e-3) / 1e12
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "M_diff block-mask attention forward calls/s (training micro-batch)",
+        "value": round(1e3 / ms, 3), "unit": "calls/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl["name"], "B": Bn, "N": N, "K": K, "blocks_per_seq": NB,
+                   "Hq": Hq, "Hkv": Hkv, "D": D, "layout": wl["layout"],
+                   "graph": not args.no_graph},
+        "timing": {"repeats": args.repeats, "statistic": "median",
+                   "ms_repeats": [round(m, 5) for m in per]},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel (blocks as requests over a shared context)",
+                     "us_per_launch": round(ms * 1e3, 3), "flops_per_launch": flops,
+                     "bytes_per_launch": nbytes, "hbm_gbps": round(gbps, 1),
+                     "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)},
+    }
+    if flops / 2.5e15 < nbytes / (HBM_PEAK_GBPS * 1e9):
+        res["roofline"].update(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS,
+                               unit="GB/s", frac=round(gbps / HBM_PEAK_GBPS, 4))
+    if not args.no_cpu:
+        import oracle
+        # the oracle on every 16th block of the first sequence, scaled by FLOPs
+        sel = list(range(NB - 1, -1, -16))
+        sub = {k: getattr(inp, k)[:1, sel].contiguous() for k in ("q", "k_blk", "v_blk")}
+        anc = inp.anchors[:1, sel].contiguous()
+        t0 = time.perf_counter()
+        oracle.mdiff_attn(sub["q"].double().numpy(), inp.k_ctx[:1].double().numpy(),
+                          inp.v_ctx[:1].double().numpy(), anc.numpy(),
+                          sub["k_blk"].double().numpy(), sub["v_blk"].double().numpy(),
+                          scale=D ** -0.5)
+        t = time.perf_counter() - t0
+        sub_flops = 4 * Hq * D * K * int((anc.long() + K).sum())
+        res["cpu_baseline"] = {"value": round(sub_flops / flops / t, 6), "unit": "calls/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "cpu_model": cpu_model(),
+                               "sample": f"fp64 oracle on {len(sel)} of {Bn * NB} blocks "
+                                         "(every 16th block of sequence 0), scaled by FLOPs"}
+    print(json.dumps(res), flush=True)
+
+
+def ceiling_main(args):
+    """Only the streaming ceiling: one launch reading one attention pass's bytes
+    at the Qwen3-8B shape (34 MB), and a long launch (537 MB)."""
+    res = {"metric": "read-only streaming ceiling of one launch", "unit": "GB/s", "n_gpus": 1,
+           "higher_is_better": True, "data": "synthetic", "dtype": "u8",
+           "config": {"workload": "stream-read"}, "launches": []}
+    for nbytes, nbuf in ((34213888, 36), (536870912, 4)):
+        res["launches"].append(stream_ceiling(nbytes, nbuf, [208, 256, 512, 1024, 2048],
+                                              steps=args.steps, warmup=args.warmup))
+    res["value"] = res["launches"][0]["best_gbps"]
     print(json.dumps(res), flush=True)
 
 

@@ -140,6 +140,48 @@ size_t orthrus_block_attn_workspace_bytes(const orthrus_cache *cache, int B,
                                           int dtype, int num_splits);
 
 /*
+ * orthrus_mdiff_attn -- the diffusion view's attention under the training
+ * block mask M_diff, forward only (summary §2.2).  A sequence carries NB
+ * blocks; block j is an anchor followed by K-1 <mask> positions.  The mask
+ * has two rules: the positions of block j see the clean AR context that
+ * precedes the block's anchor (context rows t < anchors[b][j]), and the
+ * positions of one block see each other bidirectionally (all K block rows,
+ * no other block's).
+ *
+ * For sequence b, block j, block row i, query head h (KV head g = h/(Hq/Hkv)):
+ *   keys = k_ctx rows 0..anchors[b][j]-1 of head g, then k_blk rows 0..K-1 of
+ *          block (b, j);   out, lse as in orthrus_block_attn.
+ *
+ *  k_ctx, v_ctx [B][Hkv][ctx_capacity][D] dtype: each sequence's clean context
+ *               (the AR view's keys/values, post-RoPE), read, never written
+ *  anchors      device int32 [B][NB]: 0 <= anchors[b][j] <= ctx_capacity
+ *               (caller contract, not checked on the device)
+ *  max_anchor   host upper bound on the anchors (0 = ctx_capacity); sizes the
+ *               split plan only: a wrong hint costs speed, never correctness
+ *  q, out       [B][NB][K][Hq][D] dtype
+ *  k_blk, v_blk [B][NB][K][Hkv][D] dtype: the diffusion view's block keys/values
+ *  lse          [B][NB][Hq][K] float, may be NULL
+ *  Same limits as orthrus_block_attn (K <= 64, D in {64, 128}, ...), and
+ *  B*NB <= 2^24.  workspace >= orthrus_mdiff_attn_workspace_bytes(...).
+ * Blocks are the requests of the block attention kernels, each reading its
+ * sequence's context through a shared base (no copy); they are dispatched
+ * from the last block of the last sequence, longest first when anchors grow
+ * along a sequence.
+ */
+int orthrus_mdiff_attn(const void *k_ctx, const void *v_ctx,
+                       int64_t ctx_capacity, const int32_t *anchors,
+                       int64_t max_anchor, const void *q, const void *k_blk,
+                       const void *v_blk, void *out, float *lse, int B, int NB,
+                       int K, int Hq, int Hkv, int D, int dtype, float scale,
+                       int num_splits, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+size_t orthrus_mdiff_attn_workspace_bytes(int64_t ctx_capacity,
+                                          int64_t max_anchor, int B, int NB,
+                                          int K, int Hq, int Hkv, int D,
+                                          int dtype, int num_splits);
+
+/*
  * orthrus_consensus -- greedy prediction of both views and exact
  * left-to-right consensus (summary §2.3 step 3).
  *
@@ -197,10 +239,10 @@ size_t orthrus_argmax_workspace_bytes(int64_t rows, int V, int dtype);
  *  once for R <= 256 (once per 256 rows beyond), so the call suits decode and
  *  serving batches; large R is bound by the matrix cores.  The argmax decision
  *  is taken on the fp32 accumulations: logits within a few fp32 ulps of each
- *  other may resolve differently from an exact evaluation.  Equal fp32
- *  logits go to the lowest index; the accumulation order over H is the same
- *  within each block of 128 vocabulary rows and rotates from block to block,
- *  so equal weight rows give bitwise-equal logits only inside one block.
+ *  other may resolve differently from an exact evaluation.  Every vocabulary
+ *  row goes through the same fp32 operations, so equal weight rows give
+ *  bitwise-equal logits wherever they are in V, and equal fp32 logits go to
+ *  the lowest index.
  */
 int orthrus_lmhead_argmax(const void *hidden, const void *weight, int R, int H,
                           int V, int dtype, int32_t *idx, void *workspace,
@@ -224,7 +266,9 @@ size_t orthrus_lmhead_argmax_workspace_bytes(int R, int H, int V, int dtype);
  *  k_blk, v_blk  layer 0's AR-view block rows [B][K][Hkv][D]; layer l at
  *            + l * blk_layer_stride elements
  *  n_emit    device int32 [B], each in 0..K (e.g. orthrus_consensus output)
- *  lens_out  device int32 [B]; must not alias cache->lens
+ *  lens_out  device int32 [B]; may be cache->lens itself (an in-place
+ *            advance: the rows are placed first, then a second launch writes
+ *            lens_out), or any other buffer that overlaps nothing else
  * Caller contracts: lens[b] + n_emit[b] <= capacity (CONTIGUOUS) or the
  * pages for those rows exist (PAGED).
  */
@@ -233,6 +277,21 @@ int orthrus_kv_append(const orthrus_cache *cache, const void *k_blk,
                       int32_t *lens_out, int B, int K, int Hkv, int D,
                       int dtype, int num_layers, int64_t cache_layer_stride,
                       int64_t blk_layer_stride, hipStream_t stream);
+
+/*
+ * orthrus_stream_read -- a measurement aid, not part of the decode step: reads
+ * `bytes` of device memory at `src` once, with `work_groups` work-groups each
+ * streaming one contiguous share (16-byte loads, several in flight per lane),
+ * and writes one folded word per work-group to sink[0..work_groups-1].  The
+ * time of one launch is the streaming ceiling of a read of that size with
+ * that many work-groups, on this chip, with nothing else to do: the yardstick
+ * next to which the block attention's bytes per second are read (the
+ * summary's §1 frames decoding as bound by memory bandwidth).
+ *  bytes a positive multiple of 16; src 16-byte aligned; 1 <= work_groups
+ *  <= 65535; sink device uint32 [work_groups].
+ */
+int orthrus_stream_read(const void *src, size_t bytes, int work_groups,
+                        uint32_t *sink, hipStream_t stream);
 
 /* Static string naming a status code ("ok", "null pointer", ...). */
 const char *orthrus_status_string(int status);

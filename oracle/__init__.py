@@ -10,6 +10,9 @@ of the pages it follows (see the C file's header for the source list):
 
 * ``block_attn``  -- shared-KV block attention, bidirectional (diffusion view)
   or causal (AR verification) inside the block; summary §2.1-§2.3.
+* ``mdiff_attn``  -- the training-time block mask M_diff (forward): several
+  blocks per sequence, each causal to the clean context before its anchor and
+  bidirectional inside itself; summary §2.2.
 * ``argmax_rows`` -- greedy prediction per row, lowest index on ties;
   summary §2.3 step 3.
 * ``lmhead_logits`` / ``lmhead_argmax`` -- the greedy prediction from final
@@ -68,8 +71,12 @@ def _load():
             lib.oracle_kv_append.argtypes = [P, P, I, L, I, P, I, I, P, P, P, P, P,
                                              I, I, I, I, I, I, L, L]
             lib.oracle_kv_append.restype = I
+            lib.oracle_mdiff_attn.argtypes = [P, P, P, L, P, P, P, I, I, I, I, I, I, D, P, P]
+            lib.oracle_mdiff_attn.restype = I
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = I
+            lib.oracle_set_num_threads.argtypes = [I]
+            lib.oracle_set_num_threads.restype = None
             _lib = lib
     return _lib
 
@@ -88,6 +95,11 @@ def _i32(a):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the C oracle's OpenMP loops for later calls."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def block_attn(q, k_cache, v_cache, k_blk, v_blk, lens, *, mask, scale,
@@ -116,6 +128,27 @@ def block_attn(q, k_cache, v_cache, k_blk, v_blk, lens, *, mask, scale,
                                    _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_block_attn rejected its arguments")
+    return out, lse
+
+
+def mdiff_attn(q, k_ctx, v_ctx, anchors, k_blk, v_blk, *, scale):
+    """Diffusion-view attention under the training block mask M_diff (forward),
+    in fp64.  q, k_blk, v_blk: [B, NB, K, H, D]; k_ctx, v_ctx: [B, Hkv, cap, D]
+    (the clean context of each sequence); anchors: [B, NB].  Block j of
+    sequence b sees context rows t < anchors[b, j] and its own K block rows.
+    Returns (out [B, NB, K, Hq, D], lse [B, NB, Hq, K])."""
+    q, kc, vc, kb, vb = map(_f64, (q, k_ctx, v_ctx, k_blk, v_blk))
+    anchors = _i32(anchors)
+    B, NB, K, Hq, D = q.shape
+    Hkv = kb.shape[3]
+    cap = kc.shape[2]
+    out = np.empty((B, NB, K, Hq, D), np.float64)
+    lse = np.empty((B, NB, Hq, K), np.float64)
+    rc = _load().oracle_mdiff_attn(_ptr(q), _ptr(kc), _ptr(vc), cap, _ptr(anchors), _ptr(kb),
+                                   _ptr(vb), B, NB, K, Hq, Hkv, D, float(scale), _ptr(out),
+                                   _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_mdiff_attn rejected its arguments")
     return out, lse
 
 

@@ -248,3 +248,88 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Set the number of OpenMP threads later calls use (no effect without
+ * OpenMP); the benchmark times the oracle at one thread and at all. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/*
+ * Training-time diffusion-view attention under the block mask M_diff, forward
+ * only.  [SUM] §2.2: a sequence carries several blocks; each block is an
+ * anchor (kept visible) followed by K-1 <mask> positions.  The diffusion head
+ * reads the blocks under a mask with two rules:
+ *   1. causal context: every position of block j sees the clean AR context
+ *      that precedes the block's anchor, i.e. context rows t < anchor[j];
+ *   2. bidirectional block: the positions of one block see each other, all
+ *      K of them; positions of other blocks are never seen.
+ *
+ * For sequence b, block j, block row i and query head h (KV head
+ * g = h / (Hq/Hkv)): keys = k_ctx rows 0..anchor[b][j]-1 of head g, then
+ * k_blk rows 0..K-1 of block (b, j).  s_t = scale * <q, k_t>; out = softmax
+ * weighted sum of the values; lse = log sum_t exp(s_t).
+ *
+ *  k_ctx, v_ctx  [B][Hkv][cap][D]   the clean context (AR view), per sequence
+ *  anchors       [B][NB]            anchor position of each block, 0..cap
+ *  q, out        [B][NB][K][Hq][D]
+ *  k_blk, v_blk  [B][NB][K][Hkv][D] the diffusion view's own block K/V
+ *  lse           [B][NB][Hq][K]     may be NULL
+ * Returns 0, or -1 on a bad argument (an anchor outside 0..cap).
+ */
+int oracle_mdiff_attn(const double *q, const double *k_ctx, const double *v_ctx,
+                      long cap, const int32_t *anchors, const double *k_blk,
+                      const double *v_blk, int B, int NB, int K, int Hq,
+                      int Hkv, int D, double scale, double *out, double *lse)
+{
+    if (B < 1 || NB < 1 || K < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return -1;
+    for (long x = 0; x < (long)B * NB; ++x)
+        if (anchors[x] < 0 || anchors[x] > cap) return -1;
+    const int G = Hq / Hkv;
+    const long nrows = (long)B * NB * K * Hq;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long row = 0; row < nrows; ++row) {
+        const long blk = row / ((long)K * Hq);          /* b * NB + j */
+        const int i = (int)((row / Hq) % K);
+        const int h = (int)(row % Hq);
+        const int b = (int)(blk / NB);
+        const int g = h / G;
+        const long A = anchors[blk];
+        const long n = A + K;
+        const double *qv = q + ((blk * K + i) * Hq + h) * D;
+        double *w = (double *)malloc(sizeof(double) * (size_t)n);
+        if (!w) { bad = 1; continue; }
+        /* scores: the context rows before the anchor, then the whole block */
+        for (long t = 0; t < n; ++t) {
+            const double *kr = t < A ? k_ctx + (((long)b * Hkv + g) * cap + t) * D
+                                     : k_blk + ((blk * K + (t - A)) * Hkv + g) * D;
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d) dot += qv[d] * kr[d];
+            w[t] = scale * dot;
+        }
+        double m = -INFINITY;
+        for (long t = 0; t < n; ++t) if (w[t] > m) m = w[t];
+        double denom = 0.0;
+        for (long t = 0; t < n; ++t) { w[t] = exp(w[t] - m); denom += w[t]; }
+        double *o = out + ((blk * K + i) * Hq + h) * D;
+        for (int d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (long t = 0; t < n; ++t) {
+                const double *vr = t < A ? v_ctx + (((long)b * Hkv + g) * cap + t) * D
+                                         : v_blk + ((blk * K + (t - A)) * Hkv + g) * D;
+                acc += w[t] * vr[d];
+            }
+            o[d] = acc / denom;
+        }
+        if (lse) lse[(blk * Hq + h) * K + i] = m + log(denom);
+        free(w);
+    }
+    return bad ? -1 : 0;
+}

@@ -32,7 +32,7 @@ def attn(c, **kw):
 
 def test_exports_every_declared_function():
     declared = B.header_functions()
-    assert len(declared) == 11
+    assert len(declared) >= 12
     for name in declared:
         assert hasattr(B.lib(), name), name
     assert set(declared) == set(B.SIGNATURES)
@@ -181,9 +181,6 @@ def test_kv_append_validation():
     f = B.lib().orthrus_kv_append
     base = [FAKE, FAKE, FAKE, FAKE + 4096, 1, 32, 8, 128, B.BF16, 1, 0, 0, None]
     b = list(base)
-    b[3] = FAKE    # lens_out aliases cache.lens
-    assert f(ctypes.byref(c), *b) == B.ERR_SHAPE
-    b = list(base)
     b[2] = None
     assert f(ctypes.byref(c), *b) == B.ERR_NULL
     b = list(base)
@@ -195,6 +192,49 @@ def test_kv_append_validation():
     b = list(base)
     b[9], b[10] = 2, 3        # layer stride not a multiple of 16 bytes
     assert f(ctypes.byref(c), *b) == B.ERR_UNSUPPORTED
+
+
+def test_mdiff_attn_validation():
+    f = B.lib().orthrus_mdiff_attn
+
+    def call(**kw):
+        a = dict(kc=FAKE, vc=FAKE, cap=4096, anchors=FAKE, hint=4096, q=FAKE, kb=FAKE, vb=FAKE,
+                 out=FAKE, lse=None, B=1, NB=128, K=32, Hq=32, Hkv=8, D=128, dtype=B.BF16,
+                 scale=0.088, splits=0, ws=None, wsb=0)
+        a.update(kw)
+        return f(a["kc"], a["vc"], a["cap"], a["anchors"], a["hint"], a["q"], a["kb"], a["vb"],
+                 a["out"], a["lse"], a["B"], a["NB"], a["K"], a["Hq"], a["Hkv"], a["D"],
+                 a["dtype"], a["scale"], a["splits"], a["ws"], a["wsb"], None)
+
+    assert call(kc=None) == B.ERR_NULL
+    assert call(anchors=None) == B.ERR_NULL
+    assert call(q=None) == B.ERR_NULL
+    assert call(NB=0) == B.ERR_SHAPE
+    assert call(hint=5000) == B.ERR_SHAPE           # hint beyond the context
+    assert call(cap=-1) == B.ERR_SHAPE
+    assert call(K=65) == B.ERR_UNSUPPORTED
+    assert call(D=96) == B.ERR_UNSUPPORTED
+    assert call(dtype=7) == B.ERR_DTYPE
+    assert call(q=FAKE + 8) == B.ERR_UNSUPPORTED     # misaligned
+    # 1 x 128 blocks x 8 heads fill the chip without splits: no workspace
+    assert B.lib().orthrus_mdiff_attn_workspace_bytes(4096, 4096, 1, 128, 32, 32, 8, 128,
+                                                      B.BF16, 0) == 0
+    need = B.lib().orthrus_mdiff_attn_workspace_bytes(4096, 4096, 1, 2, 32, 32, 8, 128,
+                                                      B.BF16, 0)
+    assert need > 0
+    assert call(NB=2, ws=None, wsb=0) == B.ERR_WORKSPACE
+    assert call(NB=2, ws=FAKE, wsb=need - 1) == B.ERR_WORKSPACE
+
+
+def test_stream_read_validation():
+    f = B.lib().orthrus_stream_read
+    assert f(None, 1024, 4, FAKE, None) == B.ERR_NULL
+    assert f(FAKE, 1024, 4, None, None) == B.ERR_NULL
+    assert f(FAKE, 1000, 4, FAKE, None) == B.ERR_SHAPE        # not a multiple of 16
+    assert f(FAKE, 0, 4, FAKE, None) == B.ERR_SHAPE
+    assert f(FAKE, 1024, 0, FAKE, None) == B.ERR_SHAPE
+    assert f(FAKE + 8, 1024, 4, FAKE, None) == B.ERR_UNSUPPORTED
+    assert f(FAKE, 1024, 70000, FAKE, None) == B.ERR_UNSUPPORTED
 
 
 def test_single_hip_runtime_in_process():

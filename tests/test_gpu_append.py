@@ -46,6 +46,36 @@ def test_append_multi_layer_bit_exact(paged, dtype):
     assert np.array_equal(raw(kc_d), rk) and np.array_equal(raw(vc_d), rv)
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_append_in_place_lens(paged):
+    """lens_out may be the cache's own lens: rows land where the old lengths
+    say, then the lengths advance."""
+    layers, Bn, K, Hkv, D = 2, 6, 8, 2, 128
+    lens = [0, 15, 16, 400, 77, 1000]
+    step = W.custom_step(Bn, 4, Hkv, D, K, lens, paged=paged, seed=41)
+    cshape = step.layers[0].k_cache.shape
+    gen = torch.Generator().manual_seed(2)
+    kc = torch.randn((layers, *cshape), generator=gen).to(torch.bfloat16)
+    vc = torch.randn((layers, *cshape), generator=gen).to(torch.bfloat16)
+    kb = torch.randn((layers, Bn, K, Hkv, D), generator=gen).to(torch.bfloat16)
+    vb = torch.randn((layers, Bn, K, Hkv, D), generator=gen).to(torch.bfloat16)
+    n = torch.tensor([8, 1, 4, 0, 7, 3], dtype=torch.int32)
+    kc_d, vc_d, lens_d = dev(kc), dev(vc), dev(step.lens)
+    c = api.make_cache(kc_d[0], vc_d[0], lens_d,
+                       page_table=dev(step.page_table) if paged else None)
+    say(f"append in place paged={paged}")
+    out = api.kv_append(c, dev(kb)[0], dev(vb)[0], dev(n), lens_out=lens_d, num_layers=layers,
+                        cache_layer_stride=kc[0].numel(), blk_layer_stride=kb[0].numel())
+    torch.cuda.synchronize()
+    assert out.data_ptr() == lens_d.data_ptr()
+    rk, rv, rl = oracle.kv_append(raw(kc), raw(vc), raw(kb), raw(vb), n.numpy(),
+                                  step.lens.numpy(),
+                                  layout=oracle.PAGED if paged else oracle.CONTIGUOUS,
+                                  page_table=step.page_table.numpy() if paged else None)
+    np.testing.assert_array_equal(lens_d.cpu().numpy(), rl)
+    assert np.array_equal(raw(kc_d), rk) and np.array_equal(raw(vc_d), rv)
+
+
 @pytest.mark.parametrize("cid", [1, 2])
 def test_full_step_against_oracle(cid):
     """One decode step: BIDIR pass, CAUSAL pass, consensus, append."""

@@ -11,13 +11,15 @@ import torch
 import oracle
 import workloads as W
 from ar_shared_kv_amd import api
-from gpu_util import say
+from gpu_util import record, say
 
 pytestmark = pytest.mark.gpu
 
 CASES = [
     # (name, R, H, V)
+    ("qwen3-8b-head-benched-shape", 32, 4096, 151936),
     ("qwen3-vocab", 32, 1024, 151936),
+    ("two-views-64-rows", 64, 4096, 20000),
     ("deep-H-ragged-V", 7, 4096, 1000),
     ("seventy-rows-one-128-row-block", 70, 256, 130),
     ("fifty-rows-64-row-block", 50, 512, 3000),
@@ -45,6 +47,7 @@ def check(name, h, w, got):
         else:
             assert logits[r, got[r]] >= logits[r, ref[r]] - 2 * bound[r], f"{name} row {r}"
     say(f"  {name}: {exact}/{len(ref)} rows with a clear gap, all equal")
+    record("lmhead", name, rows=len(ref), clear_gap_rows=exact, mismatches=0)
     return exact
 
 
@@ -58,17 +61,29 @@ def test_lmhead_argmax_matches_oracle(case):
     assert exact >= R // 2
 
 
-def test_lmhead_argmax_duplicate_rows_take_the_lowest_index():
-    R, H, V = 4, 512, 3000
+@pytest.mark.parametrize("R,H,rows", [
+    (4, 512, (2900, 333)),          # 32-row blocks, 8 segments; different blocks and segments
+    (4, 512, (380, 333)),           # same block, different waves
+    (50, 512, (2177, 1)),           # 64-row blocks, 4 segments (blocks 17 and 0)
+    (100, 512, (1999, 5)),          # 128-row blocks, 2 segments (blocks 15 and 0)
+    (300, 512, (4001, 7)),          # 256-row blocks, one segment
+    (32, 4096, (151935, 77777)),    # the Qwen3-8B head: the last row and one far away
+])
+def test_lmhead_argmax_duplicate_rows_take_the_lowest_index(R, H, rows):
+    V = max(rows) + 1 if max(rows) + 1 > 3000 else 3000
     h, w = W.lmhead_inputs(R, H, V, seed=11)
-    # rows 380 and 333 (one block of 128 vocabulary rows, so one accumulation
-    # order, different waves) are the same vector, aligned with hidden row 0:
-    # for row 0 they carry bitwise-equal fp32 logits, the largest of the row
+    # two weight rows in different vocabulary blocks (each block starts its
+    # walk over H at another segment) are the same vector, aligned with
+    # hidden row 0: for row 0 they must carry bitwise-equal fp32 logits, the
+    # largest of the row, and the lower index wins
     best = (h[0].float() / h[0].float().norm()).to(torch.bfloat16)
-    w[380] = best
-    w[333] = best
+    hi, lo = rows
+    w[hi] = best
+    w[lo] = best
+    say(f"lmhead duplicates R={R} H={H} rows={rows}")
     got = api.lmhead_argmax(h.cuda(), w.cuda()).cpu().numpy()
-    assert got[0] == 333
+    record("lmhead-ties", f"R={R} H={H} rows {hi}/{lo}", token=int(got[0]), expected=int(lo))
+    assert got[0] == lo
     check("duplicates", h, w, got)
 
 

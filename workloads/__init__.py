@@ -264,3 +264,49 @@ def custom_step(B: int, Hq: int, Hkv: int, D: int, K: int, lens, dtype=BF16, pag
     lay = [layer_inputs(cfg, 0, lens_t, num_pages, capacity, salt)]
     diff, ar = consensus_logits(B, K, V, p, cfg.torch_dtype, seed_of(cfg, T_LOGITS, salt=salt))
     return StepInputs(cfg, lens_t, table, num_pages, capacity, lay, diff, ar)
+
+
+T_MD_Q, T_MD_KC, T_MD_VC, T_MD_KB, T_MD_VB, T_MD_ANCH = 15, 16, 17, 18, 19, 20
+
+# The training-time block mask (M_diff) at the Qwen3-8B attention shape: a
+# micro-batch of 4 sequences of 4,096 tokens, K = 32 blocks tiling each
+# sequence (the summary's §2.2 selects blocks of length K inside a sequence;
+# tiling is the case where every position is trained once).
+MDIFF_WORKLOAD = dict(name="mdiff-qwen3-8b-4x4096", B=4, N=4096, K=32, Hq=32, Hkv=8, D=128,
+                      layout="tile")
+
+
+@dataclass
+class MdiffInputs:
+    """Inputs of one M_diff forward (CPU tensors)."""
+    q: torch.Tensor        # [B, NB, K, Hq, D]  the diffusion view's block queries
+    k_blk: torch.Tensor    # [B, NB, K, Hkv, D] its block keys
+    v_blk: torch.Tensor
+    k_ctx: torch.Tensor    # [B, Hkv, N, D]     the clean context (AR view)
+    v_ctx: torch.Tensor
+    anchors: torch.Tensor  # int32 [B, NB]
+
+
+def mdiff_anchors(B: int, N: int, K: int, NB: int, layout: str, seed: int) -> torch.Tensor:
+    """Anchor positions: "tile" puts block j at j*K (NB = N // K blocks that
+    cover the sequence); "random" draws NB positions uniformly in [0, N],
+    sorted per sequence (blocks may overlap; 0 and N are allowed)."""
+    if layout == "tile":
+        a = torch.arange(NB, dtype=torch.int32) * K
+        return a.expand(B, NB).contiguous()
+    a = torch.randint(0, N + 1, (B, NB), generator=gen(seed), dtype=torch.int64)
+    return a.sort(dim=1).values.to(torch.int32)
+
+
+def mdiff_inputs(B: int, N: int, K: int, Hq: int, Hkv: int, D: int, layout: str = "tile",
+                 NB: int = 0, dtype=BF16, seed: int = 0) -> MdiffInputs:
+    dt = _TORCH_DTYPE[dtype]
+    NB = NB or N // K
+    s = lambda tid: 1000 * 95 + tid + 100000 * seed  # noqa: E731
+    return MdiffInputs(
+        q=normal((B, NB, K, Hq, D), dt, s(T_MD_Q)),
+        k_blk=normal((B, NB, K, Hkv, D), dt, s(T_MD_KB)),
+        v_blk=normal((B, NB, K, Hkv, D), dt, s(T_MD_VB)),
+        k_ctx=normal((B, Hkv, N, D), dt, s(T_MD_KC)),
+        v_ctx=normal((B, Hkv, N, D), dt, s(T_MD_VC)),
+        anchors=mdiff_anchors(B, N, K, NB, layout, s(T_MD_ANCH)))

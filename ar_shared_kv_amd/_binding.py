@@ -57,6 +57,9 @@ SIGNATURES = {
     "orthrus_block_attn": (_I, [_CP, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                                 _P, _SZ, _P]),
     "orthrus_block_attn_workspace_bytes": (_SZ, [_CP, _I, _I, _I, _I, _I, _I, _I]),
+    "orthrus_block_attn_noalloc": (_I, [_CP, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                                        _I, _P]),
+    "orthrus_block_attn_noalloc_max_workspace": (_SZ, []),
     "orthrus_mdiff_attn": (_I, [_P, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                 _I, _I, _F, _I, _P, _SZ, _P]),
     "orthrus_mdiff_attn_workspace_bytes": (_SZ, [_I64, _I64, _I, _I, _I, _I, _I, _I, _I, _I]),
@@ -158,6 +161,19 @@ def orthrus_block_attn(cache, q, k_blk, v_blk, out, lse, B, K, Hq, Hkv, D, dtype
 def orthrus_block_attn_workspace_bytes(cache, B, K, Hq, Hkv, D, dtype, num_splits) -> int:
     return lib().orthrus_block_attn_workspace_bytes(ctypes.byref(cache), B, K, Hq, Hkv, D, dtype,
                                                     num_splits)
+
+
+def orthrus_block_attn_noalloc(cache, q, k_blk, v_blk, out, lse, B, K, Hq, Hkv, D, dtype, mask,
+                               scale, num_splits, stream=None) -> int:
+    return lib().orthrus_block_attn_noalloc(ctypes.byref(cache), ptr(q), ptr(k_blk), ptr(v_blk),
+                                            ptr(out), ptr(lse), B, K, Hq, Hkv, D, dtype, mask,
+                                            scale, num_splits,
+                                            stream if isinstance(stream, int)
+                                            else stream_handle(stream))
+
+
+def orthrus_block_attn_noalloc_max_workspace() -> int:
+    return lib().orthrus_block_attn_noalloc_max_workspace()
 
 
 def orthrus_mdiff_attn(k_ctx, v_ctx, ctx_capacity, anchors, max_anchor, q, k_blk, v_blk, out,

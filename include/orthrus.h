@@ -140,6 +140,29 @@ size_t orthrus_block_attn_workspace_bytes(const orthrus_cache *cache, int B,
                                           int dtype, int num_splits);
 
 /*
+ * orthrus_block_attn_noalloc -- orthrus_block_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments and results, without
+ * the workspace: the split partials go to a fixed array of
+ * orthrus_block_attn_noalloc_max_workspace() bytes (64 MiB) that the library
+ * holds on each GPU it runs on until the process ends.  A call whose
+ * orthrus_block_attn_workspace_bytes(...) exceeds that size returns
+ * ORTHRUS_ERR_WORKSPACE and launches nothing.  The array is looked up for
+ * the current device (hipGetDevice) on its first call there; `stream` must
+ * belong to that device.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * on it; calls ordered on one stream do not.  Nothing in it needs clearing
+ * between calls (every partial read is written by the same call first).
+ */
+int orthrus_block_attn_noalloc(const orthrus_cache *cache, const void *q,
+                               const void *k_blk, const void *v_blk, void *out,
+                               float *lse, int B, int K, int Hq, int Hkv,
+                               int D, int dtype, int mask, float scale,
+                               int num_splits, hipStream_t stream);
+
+size_t orthrus_block_attn_noalloc_max_workspace(void);
+
+/*
  * orthrus_mdiff_attn -- the diffusion view's attention under the training
  * block mask M_diff, forward only (summary §2.2).  A sequence carries NB
  * blocks; block j is an anchor followed by K-1 <mask> positions.  The mask

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "liborthrus.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "orthrus.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = range(7)
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 BIDIR, CAUSAL = 0, 1
 CONTIGUOUS, PAGED = 0, 1
 
@@ -45,6 +45,10 @@ class orthrus_cache(ctypes.Structure):
         ("max_pages_per_req", ctypes.c_int64),
         ("lens", ctypes.c_void_p),
         ("max_len", ctypes.c_int64),
+        ("kv_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -71,6 +75,14 @@ SIGNATURES = {
     "orthrus_lmhead_argmax_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "orthrus_kv_append": (_I, [_CP, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I64, _P]),
     "orthrus_stream_read": (_I, [_P, _SZ, _I, _P, _P]),
+    "orthrus_consensus_tokens": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "orthrus_gemm": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
+    "orthrus_gemm_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "orthrus_rmsnorm": (_I, [_P, _P, _P, _I, _I, _F, _P]),
+    "orthrus_qk_norm_rope": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _F, _P]),
+    "orthrus_block_tokens": (_I, [_P, _P, _I, _P, _I, _I, _P]),
+    "orthrus_swiglu": (_I, [_P, _P, _I, _I, _P]),
+    "orthrus_embed": (_I, [_P, _P, _P, _I, _I, _P]),
     "orthrus_status_string": (ctypes.c_char_p, [_I]),
     "orthrus_version": (_I, []),
 }
@@ -124,12 +136,14 @@ def stream_handle(stream=None) -> int:
     return stream.cuda_stream
 
 
-def make_cache(k, v, lens, *, page_table=None, capacity=None, max_len=0, page_size=16):
+def make_cache(k, v, lens, *, page_table=None, capacity=None, max_len=0, page_size=16,
+               k_scale=None, v_scale=None):
     """orthrus_cache for torch tensors.
 
     Contiguous: k, v [B, Hkv, cap, D].  Paged: k, v [num_pages, Hkv, page, D]
-    with page_table [B, max_pages].  The returned struct keeps references to
-    the tensors it points at.
+    with page_table [B, max_pages].  With k_scale/v_scale (fp32, the cache's
+    shape without D) the cache holds fp8 e4m3 codes (uint8 tensors).  The
+    returned struct keeps references to the tensors it points at.
     """
     c = orthrus_cache()
     if page_table is None:
@@ -144,7 +158,10 @@ def make_cache(k, v, lens, *, page_table=None, capacity=None, max_len=0, page_si
         c.max_pages_per_req = int(page_table.shape[1])
     c.k, c.v, c.lens = ptr(k), ptr(v), ptr(lens)
     c.max_len = int(max_len)
-    c._keep = (k, v, lens, page_table)
+    if k_scale is not None:
+        c.kv_dtype = FP8_E4M3
+        c.k_scale, c.v_scale = ptr(k_scale), ptr(v_scale)
+    c._keep = (k, v, lens, page_table, k_scale, v_scale)
     return c
 
 
@@ -237,6 +254,49 @@ def orthrus_kv_append(cache, k_blk, v_blk, n_emit, lens_out, B, K, Hkv, D, dtype
 def orthrus_stream_read(src, nbytes, work_groups, sink, stream=None) -> int:
     return lib().orthrus_stream_read(ptr(src), nbytes, work_groups, ptr(sink),
                                      stream if isinstance(stream, int) else stream_handle(stream))
+
+
+def _st(stream):
+    return stream if isinstance(stream, int) else stream_handle(stream)
+
+
+def orthrus_consensus_tokens(diff_tok, ar_tok, B, K, n_match, n_emit, emit_off, emitted,
+                             next_anchor, stream=None) -> int:
+    return lib().orthrus_consensus_tokens(ptr(diff_tok), ptr(ar_tok), B, K, ptr(n_match),
+                                          ptr(n_emit), ptr(emit_off), ptr(emitted),
+                                          ptr(next_anchor), _st(stream))
+
+
+def orthrus_gemm(x, w, residual, y, R, N, Kin, out_dtype, workspace, workspace_bytes,
+                 stream=None) -> int:
+    return lib().orthrus_gemm(ptr(x), ptr(w), ptr(residual), ptr(y), R, N, Kin, out_dtype,
+                              ptr(workspace), workspace_bytes, _st(stream))
+
+
+def orthrus_gemm_workspace_bytes(R, N, Kin) -> int:
+    return lib().orthrus_gemm_workspace_bytes(R, N, Kin)
+
+
+def orthrus_rmsnorm(x, weight, y, R, H, eps, stream=None) -> int:
+    return lib().orthrus_rmsnorm(ptr(x), ptr(weight), ptr(y), R, H, eps, _st(stream))
+
+
+def orthrus_qk_norm_rope(qkv, q_norm, k_norm, lens, K, q, k, v, R, Hq, Hkv, D, eps, theta,
+                         stream=None) -> int:
+    return lib().orthrus_qk_norm_rope(ptr(qkv), ptr(q_norm), ptr(k_norm), ptr(lens), K, ptr(q),
+                                      ptr(k), ptr(v), R, Hq, Hkv, D, eps, theta, _st(stream))
+
+
+def orthrus_block_tokens(anchor, cand, fill, out, B, K, stream=None) -> int:
+    return lib().orthrus_block_tokens(ptr(anchor), ptr(cand), fill, ptr(out), B, K, _st(stream))
+
+
+def orthrus_swiglu(gate_up, act, R, I, stream=None) -> int:
+    return lib().orthrus_swiglu(ptr(gate_up), ptr(act), R, I, _st(stream))
+
+
+def orthrus_embed(tokens, table, h, R, H, stream=None) -> int:
+    return lib().orthrus_embed(ptr(tokens), ptr(table), ptr(h), R, H, _st(stream))
 
 
 def orthrus_status_string(status: int) -> str:

@@ -34,7 +34,10 @@ def _need(name, t, *, dtype=None, shape=None, device=None):
     return t
 
 
-def make_cache(k, v, lens, *, page_table=None, max_len=0):
+def make_cache(k, v, lens, *, page_table=None, max_len=0, k_scale=None, v_scale=None):
+    """orthrus_cache over k, v [B, Hkv, cap, D] (or paged [pages, Hkv, 16, D]
+    with page_table [B, max_pages]).  With k_scale/v_scale (float32, the
+    cache shape without D) k and v are uint8 tensors of OCP E4M3 codes."""
     _need("k_cache", k)
     _need("v_cache", v, dtype=k.dtype, shape=k.shape, device=k.device)
     if k.dim() != 4:
@@ -44,7 +47,22 @@ def make_cache(k, v, lens, *, page_table=None, max_len=0):
         _need("page_table", page_table, dtype=torch.int32, device=k.device)
         if page_table.dim() != 2 or page_table.shape[0] != lens.shape[0]:
             raise ValueError("page_table must be [B, max_pages] with B = len(lens)")
-    return B_.make_cache(k, v, lens, page_table=page_table, max_len=max_len)
+    if (k_scale is None) != (v_scale is None):
+        raise ValueError("an E4M3 cache needs both k_scale and v_scale")
+    if k_scale is not None:
+        if k.dtype != torch.uint8:
+            raise TypeError("an E4M3 cache holds uint8 codes")
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+            _need(name, t, dtype=torch.float32, shape=k.shape[:-1], device=k.device)
+    return B_.make_cache(k, v, lens, page_table=page_table, max_len=max_len, k_scale=k_scale,
+                         v_scale=v_scale)
+
+
+def _cache_matches(cache, dtype, device, Hkv, D):
+    ck = cache._keep[0]
+    fp8 = cache.kv_dtype == B_.FP8_E4M3
+    ok = (ck.dtype == torch.uint8 and dtype == torch.bfloat16) if fp8 else ck.dtype == dtype
+    return ok and ck.device == device and ck.shape[1] == Hkv and ck.shape[3] == D
 
 
 def block_attn_workspace(cache, B, K, Hq, Hkv, D, dtype, num_splits=0, device=None):
@@ -65,8 +83,8 @@ def block_attn(q, k_blk, v_blk, cache, *, mask, scale=None, num_splits=0, out=No
     _need("q", q)
     _need("k_blk", k_blk, dtype=q.dtype, shape=(Bn, K, Hkv, D), device=q.device)
     _need("v_blk", v_blk, dtype=q.dtype, shape=(Bn, K, Hkv, D), device=q.device)
-    ck = cache._keep[0]
-    if ck.dtype != q.dtype or ck.device != q.device or ck.shape[1] != Hkv or ck.shape[3] != D:
+    if not _cache_matches(cache, q.dtype, q.device, Hkv, D):
+        ck = cache._keep[0]
         raise ValueError(f"cache {tuple(ck.shape)} {ck.dtype} does not match q/k_blk "
                          f"(Hkv={Hkv}, D={D}, {q.dtype})")
     if cache._keep[2].shape[0] != Bn:
@@ -210,9 +228,7 @@ def kv_append(cache, k_blk, v_blk, n_emit, lens_out=None, *, num_layers=1,
     _need("k_blk", k_blk)
     _need("v_blk", v_blk, dtype=k_blk.dtype, shape=k_blk.shape, device=k_blk.device)
     _need("n_emit", n_emit, dtype=torch.int32, shape=(Bn,), device=k_blk.device)
-    ck = cache._keep[0]
-    if ck.dtype != k_blk.dtype or ck.device != k_blk.device or ck.shape[1] != Hkv \
-            or ck.shape[3] != D:
+    if not _cache_matches(cache, k_blk.dtype, k_blk.device, Hkv, D):
         raise ValueError("cache and block rows differ in dtype, device, Hkv or D")
     if lens_out is None:
         lens_out = torch.empty(Bn, dtype=torch.int32, device=k_blk.device)

@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OUT = os.path.join(HERE, "liborthrus.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["abi.cpp", "block_attn.hip", "consensus.hip", "kv_append.hip", "lmhead.hip", "probe.hip", "noalloc.hip"]
+SOURCES = ["abi.cpp", "block_attn.hip", "consensus.hip", "kv_append.hip", "lmhead.hip", "probe.hip", "noalloc.hip",
+           "layers.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

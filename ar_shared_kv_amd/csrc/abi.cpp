@@ -55,6 +55,11 @@ AttnPlan plan_block_attn(const orthrus_cache *c, int B, int K, int Hq, int Hkv, 
         return pl;
     }
     if (K > 64 || (D != 64 && D != 128) || Hq / Hkv > 16) { pl.status = ORTHRUS_ERR_UNSUPPORTED; return pl; }
+    if (c->kv_dtype != 0 && c->kv_dtype != ORTHRUS_FP8_E4M3) { pl.status = ORTHRUS_ERR_DTYPE; return pl; }
+    if (c->kv_dtype == ORTHRUS_FP8_E4M3 && (dtype != ORTHRUS_BF16 || D != 128)) {
+        pl.status = ORTHRUS_ERR_UNSUPPORTED;
+        return pl;
+    }
     int64_t lmax;
     if (c->layout == ORTHRUS_LAYOUT_CONTIGUOUS) {
         if (c->capacity < 0 || c->max_len > c->capacity) { pl.status = ORTHRUS_ERR_SHAPE; return pl; }
@@ -165,6 +170,8 @@ int block_attn_impl(const orthrus_cache *cache, const void *q, const void *k_blk
     if (!cache || !q || !k_blk || !v_blk || !out) return ORTHRUS_ERR_NULL;
     if (!cache->k || !cache->v || !cache->lens) return ORTHRUS_ERR_NULL;
     if (cache->layout == ORTHRUS_LAYOUT_PAGED && !cache->page_table) return ORTHRUS_ERR_NULL;
+    if (cache->kv_dtype == ORTHRUS_FP8_E4M3 && (!cache->k_scale || !cache->v_scale))
+        return ORTHRUS_ERR_NULL;
     if (mask != ORTHRUS_MASK_BIDIR && mask != ORTHRUS_MASK_CAUSAL) return ORTHRUS_ERR_DTYPE;
     AttnPlan pl = plan_block_attn(cache, B, K, Hq, Hkv, D, dtype, num_splits);
     if (pl.status != ORTHRUS_OK) return pl.status;
@@ -206,6 +213,9 @@ int block_attn_impl(const orthrus_cache *cache, const void *q, const void *k_blk
              pl.S_grid > 1) ? 1 : 0;
     p.nbps = nbps;
     p.reverse = reverse;
+    p.kv8 = cache->kv_dtype == ORTHRUS_FP8_E4M3 ? 1 : 0;
+    p.ks = cache->k_scale;
+    p.vs = cache->v_scale;
     if (pl.S_grid > 1) {
         p.ws_o = workspace;
         p.ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.ws_lse_offset);
@@ -305,6 +315,18 @@ int orthrus_consensus(const void *diff_logits, const void *ar_logits, int B, int
                                              emit_off, emitted, next_anchor, stream));
 }
 
+int orthrus_consensus_tokens(const int32_t *diff_tok, const int32_t *ar_tok, int B, int K,
+                             int32_t *n_match, int32_t *n_emit, int32_t *emit_off,
+                             int32_t *emitted, int32_t *next_anchor, hipStream_t stream)
+{
+    if (!diff_tok || !ar_tok || !n_match || !n_emit || !emit_off || !emitted || !next_anchor)
+        return ORTHRUS_ERR_NULL;
+    if (B < 1 || K < 1) return ORTHRUS_ERR_SHAPE;
+    if (K > 64 || (int64_t)B * K > 65536) return ORTHRUS_ERR_UNSUPPORTED;
+    return map_err(launch_consensus_tokens(diff_tok, ar_tok, B, K, n_match, n_emit, emit_off,
+                                           emitted, next_anchor, stream));
+}
+
 size_t orthrus_argmax_workspace_bytes(int64_t rows, int V, int dtype)
 {
     if (rows < 1 || rows > 131072 || V < 1) return 0;
@@ -345,6 +367,13 @@ int orthrus_kv_append(const orthrus_cache *cache, const void *k_blk, const void 
         blk_layer_stride < 0)
         return ORTHRUS_ERR_SHAPE;
     if (K > 64 || (D != 64 && D != 128) || B > 8192) return ORTHRUS_ERR_UNSUPPORTED;
+    if (cache->kv_dtype != 0 && cache->kv_dtype != ORTHRUS_FP8_E4M3) return ORTHRUS_ERR_DTYPE;
+    const bool kv8 = cache->kv_dtype == ORTHRUS_FP8_E4M3;
+    if (kv8) {
+        if (!cache->k_scale || !cache->v_scale) return ORTHRUS_ERR_NULL;
+        if (dtype != ORTHRUS_BF16 || D != 128) return ORTHRUS_ERR_UNSUPPORTED;
+        if (num_layers > 1 && (cache_layer_stride % D)) return ORTHRUS_ERR_UNSUPPORTED;
+    }
     const int esize = dtype == ORTHRUS_BF16 ? 2 : 4;
     if (cache->layout == ORTHRUS_LAYOUT_CONTIGUOUS) {
         if (cache->capacity < 1) return ORTHRUS_ERR_SHAPE;
@@ -352,7 +381,9 @@ int orthrus_kv_append(const orthrus_cache *cache, const void *k_blk, const void 
         if (cache->page_size != 16) return ORTHRUS_ERR_UNSUPPORTED;
         if (cache->num_pages < 1 || cache->max_pages_per_req < 1) return ORTHRUS_ERR_SHAPE;
     }
-    if (num_layers > 1 && (((cache_layer_stride * esize) & 15) || ((blk_layer_stride * esize) & 15)))
+    const int cache_esize = kv8 ? 1 : esize;
+    if (num_layers > 1 &&
+        (((cache_layer_stride * cache_esize) & 15) || ((blk_layer_stride * esize) & 15)))
         return ORTHRUS_ERR_UNSUPPORTED;
     if (!aligned16(k_blk) || !aligned16(v_blk) || !aligned16(cache->k) || !aligned16(cache->v))
         return ORTHRUS_ERR_UNSUPPORTED;
@@ -378,6 +409,10 @@ int orthrus_kv_append(const orthrus_cache *cache, const void *k_blk, const void 
     p.cache_layer_stride = cache_layer_stride;
     p.blk_layer_stride = blk_layer_stride;
     p.lens_in_place = lens_out == cache->lens ? 1 : 0;
+    p.kv8 = kv8 ? 1 : 0;
+    p.ks = cache->k_scale;
+    p.vs = cache->v_scale;
+    p.scale_layer_stride = kv8 ? cache_layer_stride / D : 0;
     return map_err(launch_kv_append(p, stream));
 }
 

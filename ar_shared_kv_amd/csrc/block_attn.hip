@@ -62,6 +62,15 @@ __device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, ui
                  : "memory", "m0");
 }
 
+// 4-byte global -> LDS copy per active lane (lane l lands at lds + 4*l).
+__device__ __forceinline__ void lds_dma4(const void *gptr, uint32_t lds_addr) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(gptr), "s"(m0)
+                 : "memory", "m0");
+}
+
 }  // namespace
 
 // Element offset of (row r, column d) inside one split partial block of
@@ -128,7 +137,13 @@ __device__ __forceinline__ bool lpt_item(const AttnParams& p, int pos, int lane,
 // LDS DMA as part of the prologue instead of through VGPR loads.
 // Two work-groups per CU (a 2-slot ring) keep four-wave work-groups (64 rows
 // in two key slices, or 128 rows in one) within 256 registers per lane.
-template <int D, int NR, int KS, int NSTAGE, int NPRE, bool PAGED, bool QLDS>
+// FP8: the cache holds OCP e4m3 codes with one power-of-two scale per (row,
+// KV head).  Cache tiles stream into the ring as codes and scales (half the
+// bytes); once a tile has landed the work-group decodes it into one of two
+// bf16 tile buffers (code x scale is exact in bf16), and the tile is then
+// computed exactly as a bf16 one.  The block rows arrive as bf16 and go
+// straight into a tile buffer.
+template <int D, int NR, int KS, int NSTAGE, int NPRE, bool PAGED, bool QLDS, bool FP8>
 __global__ void __launch_bounds__(64 * NR * KS, (NR * KS == 4 && NSTAGE == 2) ? 2 : 1)
 attn_bf16_kernel(AttnParams p)
 {
@@ -157,16 +172,33 @@ attn_bf16_kernel(AttnParams p)
     static_assert(CK % NW == 0 && CV % NW == 0 && CQ % NW == 0, "chunks must split evenly");
     static_assert(NPRE >= 1 && NPRE < NSTAGE, "prefetch depth");
     constexpr int LK = CK / NW, LV = CV / NW, LQ = CQ / NW;
-    constexpr int LPT = LK + LV;               // DMA loads per tile per lane
+    // FP8 ring slots: K codes (TK x D bytes), V codes, then 64 K and 64 V
+    // scales (fp32); each wave moves one share of the scales with 4-byte DMAs
+    static_assert(!FP8 || (D == 128 && !QLDS && NSTAGE == NPRE + 1), "fp8 layout");
+    constexpr int K8_BYTES = TK * D, V8_BYTES = TK * D;
+    constexpr int SC_OFF = K8_BYTES + V8_BYTES;
+    constexpr int SLOT8 = SC_OFF + 1024;                  // 512 B of scales, 1 KiB aligned
+    constexpr int LK8 = K8_BYTES / 1024 / NW, LV8 = V8_BYTES / 1024 / NW;
+    constexpr int SC_LANES = 2 * TK / NW;                 // scale dwords per wave
+    static_assert(!FP8 || (LK8 * NW * 1024 == K8_BYTES && SC_LANES <= 64), "fp8 chunks");
+    constexpr int LPT = FP8 ? LK8 + LV8 + 1 : LK + LV;   // DMA loads per cache tile per lane
     static_assert(LPT * (NPRE + 1) + LQ <= 63, "vmcnt range");
     // Lazy rescaling: the running max only moves when a tile's max exceeds
     // it by more than 2^kLazy in exp2 units (weights stay <= 2^kLazy).
     constexpr float kLazy = 8.0f;
 
     constexpr int PAGE_BYTES = PAGED ? kMaxSplitPages * 4 : 0;
-    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * SLOT + Q_EXTRA + PAGE_BYTES];
-    int* s_pages = reinterpret_cast<int*>(smem + NSTAGE * SLOT + Q_EXTRA);   // PAGED only
-    constexpr int Q_OFF = QSLOT ? (NSTAGE - 1) * SLOT : NSTAGE * SLOT;
+    constexpr int RING = FP8 ? NSTAGE * SLOT8 : NSTAGE * SLOT;
+    constexpr int BF_OFF = RING;                          // FP8: two bf16 tile buffers
+    constexpr int BF_BYTES = FP8 ? 2 * SLOT : 0;
+    constexpr int LDS_TOTAL = RING + BF_BYTES + Q_EXTRA + PAGE_BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_TOTAL];
+    int* s_pages = reinterpret_cast<int*>(smem + RING + BF_BYTES + Q_EXTRA);   // PAGED only
+    constexpr int Q_OFF = QSLOT ? (NSTAGE - 1) * SLOT : RING + BF_BYTES;
+    // LDS of tile t's bf16 K and V (the ring slot, or FP8's decoded buffer)
+    auto tile_lds = [&](int t) __attribute__((always_inline)) -> char* {
+        return FP8 ? smem + BF_OFF + (t & 1) * SLOT : smem + (t % NSTAGE) * SLOT;
+    };
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -231,7 +263,9 @@ attn_bf16_kernel(AttnParams p)
     // reads; V rows by 2*(row & 3) for the transposed 8-byte reads.
     const char* kc = (const char*)p.kc;
     const char* vc = (const char*)p.vc;
-    const int64_t cont_base = ((int64_t)(b / p.nbps) * p.Hkv + g) * p.cap * D * 2;    // bytes
+    constexpr int ESZ = FP8 ? 1 : 2;                      // bytes per cache element
+    const int64_t cont_row0 = ((int64_t)(b / p.nbps) * p.Hkv + g) * p.cap;   // first cache row
+    const int64_t cont_base = cont_row0 * D * ESZ;                          // bytes
     const int64_t blk_base = ((int64_t)b * p.K * p.Hkv + g) * D * 2;
     const int blk_stride = p.Hkv * D * 2;
     // Load i of a tile by this lane (K chunks first, then V): the tile row it
@@ -259,10 +293,57 @@ attn_bf16_kernel(AttnParams p)
     int n_cache_tiles = 0;
     int last_issued = -1;      // highest tile index of the true sequence issued so far
 
+    constexpr int LPT16 = LK + LV;              // DMA loads per bf16 tile per lane
+    // FP8 cache tile t (rows start..start+count-1): codes and scales into ring
+    // slot t % NSTAGE.  Chunk i of the codes: 8 rows of 128 bytes, lane l on
+    // row 8*(i*NW + wave) + l/8, bytes 16*(l%8); scales: dword q = the wave's
+    // share, K scales of keys 0..63 then V scales (rows clamped to count-1).
+    auto issue_rows8 = [&](int t, int start, int count) __attribute__((always_inline)) {
+        const uint32_t slot_lds = lds_base + (uint32_t)((t % NSTAGE) * SLOT8);
+#pragma unroll
+        for (int i = 0; i < LK8 + LV8; ++i) {
+            const bool isv = i >= LK8;
+            const int cc = (isv ? i - LK8 : i) * NW + wave;
+            const int row = cc * 8 + lane / 8;
+            const int rowc = row < count ? row : count - 1;
+            const char* base = isv ? vc : kc;
+            const char* src;
+            if constexpr (PAGED) {
+                const int key = start + rowc;
+                const int page = s_pages[(key - kbeg) >> 4];
+                src = base + (((int64_t)page * p.Hkv + g) * 16 + (key & 15)) * D;
+            } else {
+                src = base + cont_base + (int64_t)(start + rowc) * D;
+            }
+            lds_dma16(src + 16 * (lane % 8), slot_lds + (isv ? K8_BYTES : 0) + cc * 1024);
+        }
+        if (lane < SC_LANES) {
+            const int q = wave * SC_LANES + lane;     // 0..127
+            const int key = q & (TK - 1);
+            const int rowc = key < count ? key : count - 1;
+            const float* sc = q < TK ? p.ks : p.vs;
+            int64_t e;
+            if constexpr (PAGED) {
+                const int kk = start + rowc;
+                const int page = s_pages[(kk - kbeg) >> 4];
+                e = ((int64_t)page * p.Hkv + g) * 16 + (kk & 15);
+            } else {
+                e = cont_row0 + start + rowc;
+            }
+            lds_dma4(sc + e, slot_lds + SC_OFF + (uint32_t)(wave * SC_LANES) * 4);
+        }
+    };
     // issue the global->LDS loads of tile t (rows start..start+count-1 of the
-    // cache, or the block rows) into ring slot t % NSTAGE
+    // cache, or the block rows) into ring slot t % NSTAGE (FP8: cache tiles
+    // as codes, the bf16 block rows into tile buffer t & 1)
     auto issue_rows = [&](int t, bool is_blk, int start, int count) __attribute__((always_inline)) {
-        const uint32_t slot_lds = lds_base + (uint32_t)((t % NSTAGE) * SLOT);
+        if constexpr (FP8) {
+            if (!is_blk) {
+                issue_rows8(t, start, count);
+                return;
+            }
+        }
+        const uint32_t slot_lds = lds_base + (uint32_t)(tile_lds(t) - smem);
         if (!is_blk && !PAGED && count == TK) {
             // fast path: a full contiguous tile, rows D*2 bytes apart
             const char* kt = kc + cont_base + (int64_t)start * D * 2;
@@ -271,7 +352,7 @@ attn_bf16_kernel(AttnParams p)
             // which needs no per-lane 64-bit address: 179-181 vs 184 us at
             // 131,072 keys, K = 64; the others were 1% faster without it
 #pragma unroll
-            for (int i = 0; i < LPT; ++i) {
+            for (int i = 0; i < LPT16; ++i) {
                 if constexpr (NR * 32 > 128)
                     lds_dma16_s(i >= LK ? vt : kt, (uint32_t)(lrow(i) * D * 2) + loff(i),
                                 slot_lds + ldst(i));
@@ -283,7 +364,7 @@ attn_bf16_kernel(AttnParams p)
             // full paged tile: 4 pages of 16 rows
             const int pidx = (start - kbeg) >> 4;
 #pragma unroll
-            for (int i = 0; i < LPT; ++i) {
+            for (int i = 0; i < LPT16; ++i) {
                 const int page = s_pages[pidx + (lrow(i) >> 4)];
                 const char* base = (i >= LK ? vc : kc) + ((int64_t)page * p.Hkv + g) * (16 * D * 2);
                 lds_dma16(base + (uint32_t)((lrow(i) & 15) * D * 2) + loff(i), slot_lds + ldst(i));
@@ -291,7 +372,7 @@ attn_bf16_kernel(AttnParams p)
         } else {
             // partial cache tile or the block tile: clamp rows to count-1
 #pragma unroll
-            for (int i = 0; i < LPT; ++i) {
+            for (int i = 0; i < LPT16; ++i) {
                 const bool isv = i >= LK;
                 const int rowc = lrow(i) < count ? lrow(i) : count - 1;
                 const char* src;
@@ -370,7 +451,11 @@ attn_bf16_kernel(AttnParams p)
             s_pages[i] = p.page_table[(int64_t)b * p.maxp + pg0 + i];
         __syncthreads();
     }
-    for (int t = spec; t < NPRE && t < n_tiles; ++t) issue(t);
+    // FP8: the prologue issues cache tiles only; the block tile follows the
+    // last cache tile's arrival (its tile buffer is then free), or comes
+    // first when the split has no cache rows
+    const int n_pro = FP8 && n_cache_tiles > 0 ? n_cache_tiles : n_tiles;
+    for (int t = spec; t < NPRE && t < n_pro; ++t) issue(t);
 
     f32x16 oacc[NDT];
 #pragma unroll
@@ -383,7 +468,7 @@ attn_bf16_kernel(AttnParams p)
 
     // Tile t's scores: S^T = K Q^T for this wave's key slice of ring slot t.
     auto qk = [&](int t, f32x16 (&sacc)[NBLK]) {
-        const char* Ks = smem + (t % NSTAGE) * SLOT;
+        const char* Ks = tile_lds(t);
         // operand reads first, then the MFMAs; with two 32-key blocks per wave
         // (64 keys) in halves of D, to stay within the register budget
         constexpr int KCH = NBLK > 1 ? 2 : 1;
@@ -415,10 +500,58 @@ attn_bf16_kernel(AttnParams p)
     // whose operands are then in registers, so the refill (tile t + NPRE)
     // may take the slot of tile t-1 (NSTAGE = NPRE + 1).
     static_assert(NSTAGE >= NPRE + 1, "ring slots for the tiles in flight");
+    // FP8: decode cache tile t (landed in ring slot t % NSTAGE) into its bf16
+    // tile buffer, in the swizzled layouts the K and V reads expect.  A job is
+    // 16 codes of one row of K or V: two codes at a time to fp32 (exact,
+    // subnormal codes included), times the row's power-of-two scale (exact),
+    // to bf16 (exact: at most 4 significant bits).  The scaled fp8 -> bf16
+    // conversion instruction would do it in one step, but it flushes
+    // subnormal codes to zero.
+    auto decode = [&](int t) __attribute__((always_inline)) {
+        if constexpr (FP8) {
+            const char* src = smem + (t % NSTAGE) * SLOT8;
+            char* dst = tile_lds(t);
+            constexpr int JOBS = 2 * TK * (D / 16) / (64 * NW);
+#pragma unroll
+            for (int jj = 0; jj < JOBS; ++jj) {
+                const int jb = tid + 64 * NW * jj;
+                const int isv = jb / (TK * (D / 16));
+                const int r = (jb / (D / 16)) % TK;
+                const int u = jb % (D / 16);
+                const u32x4 code = *(const u32x4*)(src + isv * K8_BYTES + r * D + 16 * u);
+                const float sc = *(const float*)(src + SC_OFF + 4 * (isv * TK + r));
+                u32x4 lo, hi;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const f32x2 fa = __builtin_amdgcn_cvt_pk_f32_fp8(code[w], false);
+                    const f32x2 fb = __builtin_amdgcn_cvt_pk_f32_fp8(code[w], true);
+                    const uint32_t a = pack_bf16x2(fa[0] * sc, fa[1] * sc);
+                    const uint32_t bb = pack_bf16x2(fb[0] * sc, fb[1] * sc);
+                    if (w < 2) { lo[2 * w] = a; lo[2 * w + 1] = bb; }
+                    else { hi[2 * (w - 2)] = a; hi[2 * (w - 2) + 1] = bb; }
+                }
+                const int g0 = 2 * u, g1 = 2 * u + 1;
+                const int s0 = isv ? g0 ^ (2 * (r & 3)) : g0 ^ (r & (GPR - 1));
+                const int s1 = isv ? g1 ^ (2 * (r & 3)) : g1 ^ (r & (GPR - 1));
+                char* row = dst + isv * K_BYTES + r * D * 2;
+                *(u32x4*)(row + 16 * s0) = lo;
+                *(u32x4*)(row + 16 * s1) = hi;
+            }
+        }
+    };
     auto arrive = [&](int t) __attribute__((always_inline)) {
         wait_tiles(last_issued - t);
         __syncthreads();
-        if (t + NPRE < n_tiles) issue(t + NPRE);
+        if constexpr (FP8) {
+            if (t + NPRE < n_cache_tiles) issue(t + NPRE);
+            if (t + 1 == n_cache_tiles && t + 1 < n_tiles) issue(t + 1);   // the block tile
+            if (t < n_cache_tiles) {
+                decode(t);
+                __syncthreads();
+            }
+        } else {
+            if (t + NPRE < n_tiles) issue(t + NPRE);
+        }
     };
 
     arrive(0);
@@ -540,17 +673,21 @@ attn_bf16_kernel(AttnParams p)
     const int n_fast = n_full - 1 - NPRE > 0 ? n_full - 1 - NPRE : 0;
     int t = 0;
     for (; t < n_fast; ++t) {
-        tile(t, (const uint16_t*)(smem + (t % NSTAGE) * SLOT + K_BYTES), false, TK);
+        tile(t, (const uint16_t*)(tile_lds(t) + K_BYTES), false, TK);
         // arrive(t + 1): NPRE - 1 later tiles may fly; refill tile t + 1 + NPRE
         __builtin_amdgcn_s_waitcnt(vmcnt_encode((NPRE - 1) * LPT));
         __syncthreads();
         issue_rows(t + 1 + NPRE, false, kbeg + (t + 1 + NPRE) * TK, TK);
         last_issued = t + 1 + NPRE;
+        if constexpr (FP8) {
+            decode(t + 1);
+            __syncthreads();
+        }
         qk(t + 1, scur);
     }
     for (; t < n_loop; ++t) {
 
-        const uint16_t* Vs = (const uint16_t*)(smem + (t % NSTAGE) * SLOT + K_BYTES);
+        const uint16_t* Vs = (const uint16_t*)(tile_lds(t) + K_BYTES);
         const bool is_blk = t >= n_cache_tiles;
         const int start = is_blk ? 0 : kbeg + t * TK;
         const int count = is_blk ? p.K : (kend - start < TK ? kend - start : TK);
@@ -576,7 +713,7 @@ attn_bf16_kernel(AttnParams p)
     if constexpr (KS > 1) {
         static_assert(KS == 2 && NDT % 2 == 0, "two key slices, even number of D tiles");
         constexpr int REC = HALF_DT * 16 + 4;             // floats per lane record
-        static_assert(NR * 2 * 64 * REC * 4 <= NSTAGE * SLOT, "merge buffer");
+        static_assert(NR * 2 * 64 * REC * 4 <= RING + BF_BYTES, "merge buffer");
         __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));
         __syncthreads();   // all waves are done with the ring; reuse it
         float* base = reinterpret_cast<float*>(smem) + rg * 2 * 64 * REC;
@@ -650,7 +787,7 @@ attn_bf16_kernel(AttnParams p)
     // LDS ([row][D] with a 16-byte pad) so that the output stores are whole
     // 16-byte pieces of rows.
     constexpr int RSTR = D * 2 + 16;                        // staged row stride, bytes
-    static_assert(QROWS * RSTR <= NSTAGE * SLOT, "staging buffer");
+    static_assert(QROWS * RSTR <= RING + BF_BYTES, "staging buffer");
     __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));
     __syncthreads();                                        // ring (or merge buffer) free
     char* stage = smem;
@@ -1043,7 +1180,7 @@ static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
     if (p.layout == 1) {
         constexpr int NS = ring_depth(D, NR, true, QLDS);
         constexpr int NP = prefetch_depth(D, NR, KS, NS, QLDS);
-        hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, NS, NP, true, QLDS>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, NS, NP, true, QLDS, false>), grid, block, 0, st, p);
     } else if ((NR <= 2 && (NR == 2 || (int64_t)grid.x * grid.y > 256)) || (NR == 4 && KS == 1)) {
         // Contiguous 64-row work-groups, and 32-row ones when the grid has
         // more work-groups than CUs: a 2-slot ring, one tile in flight while
@@ -1055,12 +1192,25 @@ static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
         // K = 8: 32.0 vs 36.2 us).  128-row work-groups come here as four
         // waves (KS = 1) when they outnumber the CUs.
         if constexpr (NR <= 2 || (NR == 4 && KS == 1))
-            hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, 2, 1, false, QLDS>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, 2, 1, false, QLDS, false>), grid, block, 0, st, p);
     } else {
         constexpr int NS = ring_depth(D, NR, false, QLDS);
         constexpr int NP = prefetch_depth(D, NR, KS, NS, false);
-        hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, NS, NP, false, QLDS>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, NR, KS, NS, NP, false, QLDS, false>), grid, block, 0, st, p);
     }
+    return hipGetLastError();
+}
+
+// fp8 cache (head_dim 128): a 3-slot ring of codes, two tiles in flight, the
+// query in registers, one work-group per CU
+template <int NR, int KS>
+static hipError_t launch_fp8(const AttnParams& p, hipStream_t st) {
+    dim3 grid(p.S_grid * p.B * p.Hkv, p.row_blocks);
+    dim3 block(64 * NR * KS);
+    if (p.layout == 1)
+        hipLaunchKernelGGL((attn_bf16_kernel<128, NR, KS, 3, 2, true, false, true>), grid, block, 0, st, p);
+    else
+        hipLaunchKernelGGL((attn_bf16_kernel<128, NR, KS, 3, 2, false, false, true>), grid, block, 0, st, p);
     return hipGetLastError();
 }
 
@@ -1086,6 +1236,17 @@ static void launch_merge(const AttnParams& p, dim3 grid, hipStream_t st) {
 
 template <int D>
 static hipError_t launch_bf16_d(const AttnParams& p, hipStream_t st) {
+    if (p.kv8) {
+        if constexpr (D == 128) {
+            switch (p.rows_per_wg) {
+                case 32: return launch_fp8<1, 2>(p, st);
+                case 64: return launch_fp8<2, 2>(p, st);
+                case 128: return launch_fp8<4, 2>(p, st);
+                default: return launch_fp8<8, 1>(p, st);
+            }
+        }
+        return hipErrorInvalidValue;
+    }
     switch (p.rows_per_wg) {
         case 32: return launch_bf16<D, 1, 2, true>(p, st);
         case 64: return launch_bf16<D, 2, 2, true>(p, st);

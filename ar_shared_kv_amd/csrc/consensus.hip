@@ -278,6 +278,19 @@ hipError_t launch_argmax_finalize(const uint64_t *ws, int64_t rows, int chunks, 
     return hipGetLastError();
 }
 
+hipError_t launch_consensus_tokens(const int32_t *diff_tok, const int32_t *ar_tok, int B, int K,
+                                  int32_t *n_match, int32_t *n_emit, int32_t *emit_off,
+                                  int32_t *emitted, int32_t *next_anchor, hipStream_t st)
+{
+    // the tokens are given: only the consensus pass (which reads, never
+    // writes, diff_tok and ar_tok when its TOKENS flag is off)
+    hipLaunchKernelGGL(consensus_finalize_kernel<false>, dim3(1), dim3(1024), 0, st,
+                       (const uint64_t *)nullptr, 0, B, K, const_cast<int32_t *>(diff_tok),
+                       const_cast<int32_t *>(ar_tok), n_match, n_emit, emit_off, emitted,
+                       next_anchor);
+    return hipGetLastError();
+}
+
 hipError_t launch_consensus_finalize(const uint64_t *ws, int B, int K, int chunks,
                                      int32_t *diff_tok, int32_t *ar_tok, int32_t *n_match,
                                      int32_t *n_emit, int32_t *emit_off, int32_t *emitted,

@@ -36,6 +36,8 @@ struct AttnParams {
                                       // contiguous cache of sequence b / nbps (1 = its own)
     int reverse;                      // dispatch requests from the last one (longest first
                                       // when lengths grow with the request index)
+    int kv8;                          // cache holds e4m3 codes (kc, vc) with per-row scales
+    const float *ks, *vs;             // kv8: scale of each cache row, laid out like the rows
 };
 
 int attn_rows_per_wg(int dtype, int M);
@@ -48,6 +50,9 @@ hipError_t launch_argmax_partial(const void *logits0, const void *logits1, int64
                                  hipStream_t st);
 hipError_t launch_argmax_finalize(const uint64_t *ws, int64_t rows, int chunks, int32_t *idx,
                                   hipStream_t st);
+hipError_t launch_consensus_tokens(const int32_t *diff_tok, const int32_t *ar_tok, int B, int K,
+                                  int32_t *n_match, int32_t *n_emit, int32_t *emit_off,
+                                  int32_t *emitted, int32_t *next_anchor, hipStream_t st);
 hipError_t launch_consensus_finalize(const uint64_t *ws, int B, int K, int chunks,
                                      int32_t *diff_tok, int32_t *ar_tok, int32_t *n_match,
                                      int32_t *n_emit, int32_t *emit_off, int32_t *emitted,
@@ -62,6 +67,9 @@ struct AppendParams {
     int B, K, Hkv, D, esize, layers, layout;
     int64_t cap, maxp, cache_layer_stride, blk_layer_stride;   // elements
     int lens_in_place;                // lens_out == lens: a second launch advances lens
+    int kv8;                          // the cache holds e4m3 codes: quantize the rows
+    float *ks, *vs;                   // kv8: per-row scales (layer l at + l * scale_layer_stride)
+    int64_t scale_layer_stride;
 };
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t st);
 

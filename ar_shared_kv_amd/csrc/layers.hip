@@ -1,0 +1,399 @@
+// The decode step around the Orthrus kernels: the Transformer layers that
+// produce the block attention's inputs and consume its output, for one block
+// of rows of either view (summary §2.3 steps 1-2: the diffusion head projects
+// K candidates in one pass, the frozen AR head verifies them in one pass).
+// A Qwen3-style layer: RMSNorm -> QKV projection -> per-head RMSNorm on q and
+// k -> rotary position embedding -> block attention -> output projection +
+// residual -> RMSNorm -> SwiGLU MLP + residual.  The residual stream is fp32;
+// the matrices and the projections' inputs are bf16.
+//
+// gemm_kernel: y[r][n] = sum_k x[r][k] * w[n][k] for the few rows of a
+// decode block (R = B*K) against a weight of N rows: HBM-bound (the weight
+// is read once), so the weight streams HBM -> LDS with global_load_lds
+// through a 3-slot ring, like the LM head.  A work-group covers 128 weight
+// rows and RB hidden rows; when the N/128 blocks cannot fill the chip the
+// input dimension is split S ways (S depends on N and the input size only)
+// and a second launch adds the fp32 partial sums in split order.  Every
+// output element thus goes through the same operations whatever R is: a row
+// computed in a block of 32 equals the same row computed alone.
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include "../../include/orthrus.h"
+
+namespace orthrus {
+namespace {
+
+constexpr int kGemmNB = 128;                  // weight rows per work-group
+constexpr int kGemmHC = 64;                   // input columns per chunk
+constexpr int kGemmTargetWG = 512;            // split-K aims at this many work-groups
+
+__device__ __forceinline__ void g_dma16(const void* gptr, uint32_t lds_addr) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(m0)
+                 : "memory", "m0");
+}
+
+// out_mode: 0 fp32 partial (split s of S) to part[s][R][N]; 1 fp32 y (+ res);
+// 2 bf16 y (+ res)
+template <int NSTAGE, int RB>
+__global__ void __launch_bounds__(256, 2)
+gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int R, int N, int Kin,
+            int cps, int out_mode, float* __restrict__ part, void* __restrict__ y,
+            const float* __restrict__ res)
+{
+    constexpr int HC = kGemmHC;
+    constexpr int WB = kGemmNB * HC * 2;
+    constexpr int XB = RB * HC * 2;
+    constexpr int NB = RB / 32;
+    constexpr int SLOT = WB + XB;
+    constexpr int GR = HC / 8;
+    constexpr int RPP = 1024 / (HC * 2);
+    constexpr int LOADS = SLOT / 4096;
+    constexpr int NPRE = NSTAGE - 1;
+    static_assert(SLOT % 4096 == 0 && LOADS * NSTAGE <= 63, "ring");
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * SLOT];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int half = lane >> 5;
+    const int n0 = blockIdx.x * kGemmNB;
+    const int r0 = blockIdx.y * RB;
+    const int sp = blockIdx.z;
+    const int c_lo = sp * cps;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(ORTHRUS_LDS void*)&smem[0];
+
+    auto issue = [&](int c) __attribute__((always_inline)) {
+        const uint32_t slot = lds_base + (uint32_t)((c % NSTAGE) * SLOT);
+        const int col = (c_lo + c) * HC;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int k = i * 4 + wave;
+            const bool isx = k >= WB / 1024;
+            const int row = (isx ? k - WB / 1024 : k) * RPP + lane / GR;
+            const int gsrc = (lane % GR) ^ (row % GR);
+            const uint16_t* src;
+            if (isx) {
+                const int rr = r0 + row < R ? r0 + row : R - 1;
+                src = x + (int64_t)rr * Kin + col + gsrc * 8;
+            } else {
+                const int nn = n0 + row < N ? n0 + row : N - 1;
+                src = w + (int64_t)nn * Kin + col + gsrc * 8;
+            }
+            g_dma16(src, slot + (uint32_t)(k * 1024));
+        }
+    };
+    auto wait_chunk = [&](int c) __attribute__((always_inline)) {
+        const int later = cps - 1 - c;
+        const int pend = later < NPRE - 1 ? later : NPRE - 1;
+        switch (pend) {
+            case 0: __builtin_amdgcn_s_waitcnt(vmcnt_encode(0)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(vmcnt_encode(LOADS)); break;
+            default: __builtin_amdgcn_s_waitcnt(vmcnt_encode(2 * LOADS)); break;
+        }
+    };
+    static_assert(NPRE - 1 <= 2, "wait_chunk covers up to 2 later chunks");
+
+    f32x16 acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = f32x16{};
+    const int wrow = wave * 32 + (lane & 31);
+    for (int c = 0; c < NPRE && c < cps; ++c) issue(c);
+    for (int c = 0; c < cps; ++c) {
+        wait_chunk(c);
+        __syncthreads();
+        if (c + NPRE < cps) issue(c + NPRE);
+        const char* Ws = smem + (c % NSTAGE) * SLOT;
+        const char* Xs = Ws + WB;
+        u32x4 af[HC / 16], bfr[NB][HC / 16];
+#pragma unroll
+        for (int ds = 0; ds < HC / 16; ++ds) {
+            const int g = 2 * ds + half;
+            af[ds] = *(const u32x4*)(Ws + wrow * (HC * 2) + ((g ^ (wrow % GR)) * 16));
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int xrow = 32 * j + (lane & 31);
+                bfr[j][ds] = *(const u32x4*)(Xs + xrow * (HC * 2) + ((g ^ (xrow % GR)) * 16));
+            }
+        }
+#pragma unroll
+        for (int ds = 0; ds < HC / 16; ++ds)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, af[ds]), __builtin_bit_cast(bf16x8, bfr[j][ds]),
+                    acc[j], 0, 0, 0);
+    }
+    // acc[j][i]: weight row n0 + 32*wave + 8*(i/4) + 4*half + i%4, hidden row
+    // r0 + 32*j + lane%32; four consecutive outputs per store
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int r = r0 + 32 * j + (lane & 31);
+        if (r >= R) continue;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int n = n0 + wave * 32 + 8 * q4 + 4 * half;
+            if (n >= N) continue;
+            f32x4 v = {acc[j][4 * q4], acc[j][4 * q4 + 1], acc[j][4 * q4 + 2], acc[j][4 * q4 + 3]};
+            const int64_t o = (int64_t)r * N + n;
+            if (out_mode == 0) {
+                *(f32x4*)(part + (int64_t)sp * R * N + o) = v;
+            } else {
+                if (res) v += *(const f32x4*)(res + o);
+                if (out_mode == 1) *(f32x4*)((float*)y + o) = v;
+                else *(u32x2*)((uint16_t*)y + o) = u32x2{pack_bf16x2(v[0], v[1]),
+                                                          pack_bf16x2(v[2], v[3])};
+            }
+        }
+    }
+}
+
+// y = (res +) sum over s = 0..S-1 of part[s], in that order; fp32 or bf16.
+__global__ void __launch_bounds__(256)
+gemm_reduce_kernel(const float* __restrict__ part, int S, int64_t RN4, int out_bf16,
+                   void* __restrict__ y, const float* __restrict__ res)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= RN4) return;
+    f32x4 v = ((const f32x4*)part)[i];
+    for (int s = 1; s < S; ++s) v += ((const f32x4*)part)[(int64_t)s * RN4 + i];
+    if (res) v = ((const f32x4*)res)[i] + v;
+    if (out_bf16) ((u32x2*)y)[i] = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    else ((f32x4*)y)[i] = v;
+}
+
+int gemm_splits(int N, int Kin)
+{
+    const int nblk = (N + kGemmNB - 1) / kGemmNB;
+    const int chunks = Kin / kGemmHC;
+    int S = 1;
+    while ((int64_t)nblk * S * 2 <= kGemmTargetWG && chunks % (S * 2) == 0 && chunks / (S * 2) >= 4)
+        S *= 2;
+    return S;
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * w, one work-group per row; the sum
+// of squares is reduced in a fixed order (per-thread runs, then lanes, then
+// waves), so a row's result does not depend on the other rows.
+__global__ void __launch_bounds__(256)
+rmsnorm_kernel(const float* __restrict__ x, const uint16_t* __restrict__ w, uint16_t* __restrict__ y,
+               int H, float eps)
+{
+    const float* xr = x + (int64_t)blockIdx.x * H;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < H; i += 256) ss += xr[i] * xr[i];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    __shared__ float part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+    const float inv = 1.f / sqrtf(tot / (float)H + eps);
+    uint16_t* yr = y + (int64_t)blockIdx.x * H;
+    for (int i = threadIdx.x; i < H; i += 256) {
+        const float v = xr[i] * inv * bf16_bits_to_f32(w[i]);
+        yr[i] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
+    }
+}
+
+// ------------------------------------------------------ QK norm + rotary
+// From the fp32 QKV projection [R][(Hq + 2 Hkv) * D] of the block rows (row
+// r is row r % K of request r / K, at position lens[r / K] + r % K): q and k
+// heads get RMSNorm over D (weights wq / wk), then the rotary
+// embedding with pairs (d, d + D/2) rotated by pos * theta^(-2d/D); v heads
+// are copied.  One wave per (row, head), D = 128 (lane l holds d = l and
+// l + 64).  Angles in fp64.
+__global__ void __launch_bounds__(256)
+qk_norm_rope_kernel(const float* __restrict__ qkv, const uint16_t* __restrict__ wq,
+                    const uint16_t* __restrict__ wk, const int32_t* __restrict__ lens, int K,
+                    uint16_t* __restrict__ q, uint16_t* __restrict__ k, uint16_t* __restrict__ v,
+                    int R, int Hq, int Hkv, float eps, double log_theta)
+{
+    constexpr int D = 128;
+    const int heads = Hq + 2 * Hkv;
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= R * heads) return;
+    const int lane = threadIdx.x & 63;
+    const int r = item / heads;
+    const int h = item % heads;
+    const float* src = qkv + (int64_t)r * heads * D + (int64_t)h * D;
+    float x0 = src[lane], x1 = src[lane + 64];
+    if (h >= Hq + Hkv) {                              // v: a copy
+        uint16_t* dst = v + ((int64_t)r * Hkv + (h - Hq - Hkv)) * D;
+        dst[lane] = (uint16_t)(pack_bf16x2(x0, 0.f) & 0xffffu);
+        dst[lane + 64] = (uint16_t)(pack_bf16x2(x1, 0.f) & 0xffffu);
+        return;
+    }
+    float ss = x0 * x0 + x1 * x1;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    const float inv = 1.f / sqrtf(ss / (float)D + eps);
+    const uint16_t* wn = h < Hq ? wq : wk;
+    const float n0 = x0 * inv * bf16_bits_to_f32(wn[lane]);
+    const float n1 = x1 * inv * bf16_bits_to_f32(wn[lane + 64]);
+    const double freq = exp(-(2.0 * lane / D) * log_theta);
+    double sn, cs;
+    const int pos = lens[r / K] + r % K;
+    sincos((double)pos * freq, &sn, &cs);
+    const float c = (float)cs, s = (float)sn;
+    const float o0 = n0 * c - n1 * s;
+    const float o1 = n1 * c + n0 * s;
+    uint16_t* dst = h < Hq ? q + ((int64_t)r * Hq + h) * D : k + ((int64_t)r * Hkv + (h - Hq)) * D;
+    dst[lane] = (uint16_t)(pack_bf16x2(o0, 0.f) & 0xffffu);
+    dst[lane + 64] = (uint16_t)(pack_bf16x2(o1, 0.f) & 0xffffu);
+}
+
+// ---------------------------------------------------------------- SwiGLU
+// act[r][i] = silu(gu[r][i]) * gu[r][I + i], silu(g) = g / (1 + e^-g).
+__global__ void __launch_bounds__(256)
+swiglu_kernel(const float* __restrict__ gu, uint16_t* __restrict__ act, int I, int64_t total)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= total) return;
+    const int64_t r = t / I;
+    const int i = (int)(t % I);
+    const float g = gu[r * 2 * I + i];
+    const float u = gu[r * 2 * I + I + i];
+    const float a = g / (1.f + expf(-g)) * u;
+    act[t] = (uint16_t)(pack_bf16x2(a, 0.f) & 0xffffu);
+}
+
+// ----------------------------------------------------- block input tokens
+// out[b][0] = anchor[b]; out[b][i] = cand[b][i-1] (the AR view's block: the
+// anchor then the first K-1 candidates) or, with no cand, the fill token
+// (the diffusion view's block: the anchor then <mask> tokens).
+__global__ void __launch_bounds__(256)
+block_tokens_kernel(const int32_t* __restrict__ anchor, const int32_t* __restrict__ cand,
+                    int32_t fill, int32_t* __restrict__ out, int B, int K)
+{
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= B * K) return;
+    const int b = t / K, i = t % K;
+    out[t] = i == 0 ? anchor[b] : (cand ? cand[b * K + i - 1] : fill);
+}
+
+// ------------------------------------------------------------- embedding
+__global__ void __launch_bounds__(256)
+embed_kernel(const int32_t* __restrict__ tok, const uint16_t* __restrict__ table,
+             float* __restrict__ h, int H)
+{
+    const uint16_t* row = table + (int64_t)tok[blockIdx.x] * H;
+    float* out = h + (int64_t)blockIdx.x * H;
+    for (int i = threadIdx.x; i < H; i += 256) out[i] = bf16_bits_to_f32(row[i]);
+}
+
+}  // namespace
+}  // namespace orthrus
+
+using namespace orthrus;
+
+extern "C" {
+
+size_t orthrus_gemm_workspace_bytes(int R, int N, int Kin)
+{
+    if (R < 1 || N < 1 || Kin < kGemmHC || Kin % kGemmHC || N % 4) return 0;
+    const int S = gemm_splits(N, Kin);
+    return S > 1 ? (size_t)S * R * N * sizeof(float) : 0;
+}
+
+int orthrus_gemm(const void *x, const void *w, const float *residual, void *y, int R, int N,
+                 int Kin, int out_dtype, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream)
+{
+    if (!x || !w || !y) return ORTHRUS_ERR_NULL;
+    if (out_dtype != ORTHRUS_F32 && out_dtype != ORTHRUS_BF16) return ORTHRUS_ERR_DTYPE;
+    if (R < 1 || N < 1 || Kin < 1) return ORTHRUS_ERR_SHAPE;
+    if (Kin % kGemmHC || N % 4 || R > 65535 * 128 || N > (1 << 28) / 1) return ORTHRUS_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(x) & 15u) || (reinterpret_cast<uintptr_t>(w) & 15u) ||
+        (reinterpret_cast<uintptr_t>(y) & 15u) || (reinterpret_cast<uintptr_t>(residual) & 15u))
+        return ORTHRUS_ERR_UNSUPPORTED;
+    const int S = gemm_splits(N, Kin);
+    const size_t need = S > 1 ? (size_t)S * R * N * sizeof(float) : 0;
+    if (need && (!workspace || workspace_bytes < need ||
+                 (reinterpret_cast<uintptr_t>(workspace) & 15u)))
+        return ORTHRUS_ERR_WORKSPACE;
+    const int cps = Kin / kGemmHC / S;
+    const int mode = S > 1 ? 0 : (out_dtype == ORTHRUS_F32 ? 1 : 2);
+    const uint16_t *xp = static_cast<const uint16_t *>(x), *wp = static_cast<const uint16_t *>(w);
+    float *part = static_cast<float *>(workspace);
+    const unsigned gx = (unsigned)((N + kGemmNB - 1) / kGemmNB);
+    if (R <= 32)
+        hipLaunchKernelGGL((gemm_kernel<3, 32>), dim3(gx, 1, S), dim3(256), 0, stream, xp, wp, R,
+                           N, Kin, cps, mode, part, y, residual);
+    else if (R <= 64)
+        hipLaunchKernelGGL((gemm_kernel<3, 64>), dim3(gx, 1, S), dim3(256), 0, stream, xp, wp, R,
+                           N, Kin, cps, mode, part, y, residual);
+    else
+        hipLaunchKernelGGL((gemm_kernel<2, 128>), dim3(gx, (unsigned)((R + 127) / 128), S),
+                           dim3(256), 0, stream, xp, wp, R, N, Kin, cps, mode, part, y, residual);
+    if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
+    if (S > 1) {
+        const int64_t rn4 = (int64_t)R * N / 4;
+        hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((rn4 + 255) / 256)), dim3(256), 0,
+                           stream, part, S, rn4, out_dtype == ORTHRUS_BF16 ? 1 : 0, y, residual);
+        if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
+    }
+    return ORTHRUS_OK;
+}
+
+int orthrus_rmsnorm(const float *x, const void *weight, void *y, int R, int H, float eps,
+                    hipStream_t stream)
+{
+    if (!x || !weight || !y) return ORTHRUS_ERR_NULL;
+    if (R < 1 || H < 1 || !(eps > 0.f)) return ORTHRUS_ERR_SHAPE;
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)R), dim3(256), 0, stream, x,
+                       static_cast<const uint16_t *>(weight), static_cast<uint16_t *>(y), H, eps);
+    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+int orthrus_qk_norm_rope(const float *qkv, const void *q_norm, const void *k_norm,
+                         const int32_t *lens, int K, void *q, void *k, void *v, int R, int Hq,
+                         int Hkv, int D, float eps, float rope_theta, hipStream_t stream)
+{
+    if (!qkv || !q_norm || !k_norm || !lens || !q || !k || !v) return ORTHRUS_ERR_NULL;
+    if (R < 1 || K < 1 || R % K || Hq < 1 || Hkv < 1 || !(eps > 0.f) || !(rope_theta > 1.f))
+        return ORTHRUS_ERR_SHAPE;
+    if (D != 128) return ORTHRUS_ERR_UNSUPPORTED;
+    const int64_t items = (int64_t)R * (Hq + 2 * Hkv);
+    hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, stream,
+                       qkv, static_cast<const uint16_t *>(q_norm),
+                       static_cast<const uint16_t *>(k_norm), lens, K,
+                       static_cast<uint16_t *>(q), static_cast<uint16_t *>(k),
+                       static_cast<uint16_t *>(v), R, Hq, Hkv, eps, std::log((double)rope_theta));
+    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+int orthrus_swiglu(const float *gate_up, void *act, int R, int I, hipStream_t stream)
+{
+    if (!gate_up || !act) return ORTHRUS_ERR_NULL;
+    if (R < 1 || I < 1) return ORTHRUS_ERR_SHAPE;
+    const int64_t total = (int64_t)R * I;
+    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       gate_up, static_cast<uint16_t *>(act), I, total);
+    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+int orthrus_block_tokens(const int32_t *anchor, const int32_t *cand, int32_t fill,
+                         int32_t *out, int B, int K, hipStream_t stream)
+{
+    if (!anchor || !out) return ORTHRUS_ERR_NULL;
+    if (B < 1 || K < 1) return ORTHRUS_ERR_SHAPE;
+    hipLaunchKernelGGL(block_tokens_kernel, dim3((unsigned)((B * K + 255) / 256)), dim3(256), 0,
+                       stream, anchor, cand, fill, out, B, K);
+    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+int orthrus_embed(const int32_t *tokens, const void *table, float *h, int R, int H,
+                  hipStream_t stream)
+{
+    if (!tokens || !table || !h) return ORTHRUS_ERR_NULL;
+    if (R < 1 || H < 1) return ORTHRUS_ERR_SHAPE;
+    hipLaunchKernelGGL(embed_kernel, dim3((unsigned)R), dim3(256), 0, stream, tokens,
+                       static_cast<const uint16_t *>(table), h, H);
+    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+}  // extern "C"

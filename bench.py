@@ -103,6 +103,13 @@ def parse():
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="only measure the read-only streaming ceiling of one launch "
                          "(34 MB and 537 MB per launch, distinct buffers back to back)")
+    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
+                    help="KV-cache element type: bf16, or OCP E4M3 codes with a power-of-two "
+                         "scale per row and head (half the cache bytes)")
+    ap.add_argument("--decode-step", action="store_true",
+                    help="time one whole Orthrus decode step of a 36-layer random-weight "
+                         "Qwen3-8B-shaped model (both views' passes with every layer, fused "
+                         "LM-head argmax, consensus, append) at L=8192, K=32")
     ap.add_argument("--mdiff", action="store_true",
                     help="time the training-time block-mask (M_diff) attention forward on a "
                          "4 x 4,096-token micro-batch at the Qwen3-8B shape instead")
@@ -118,12 +125,13 @@ def log(*a):
 class Step:
     """Device-resident inputs and outputs of one decode step of a workload."""
 
-    def __init__(self, cfg, splits, sets=0, draws=0, dev="cuda"):
+    def __init__(self, cfg, splits, sets=0, draws=0, dev="cuda", kv="bf16"):
         import torch
         import workloads as W
         from ar_shared_kv_amd import api
         self.cfg = cfg
         self.splits = splits
+        self.kv8 = kv == "fp8"
         nl = cfg.layers
         st = W.step_inputs(cfg, layers=1, with_logits=True)   # shapes + logits + lens
         # Input sets cycled by consecutive steps, so that a small workload's
@@ -145,8 +153,12 @@ class Step:
         self.page_table = st.page_table.to(dev) if cfg.paged else None
         cshape = tuple(st.layers[0].k_cache.shape)
         dt = cfg.torch_dtype
-        self.kc = torch.empty((nt, *cshape), dtype=dt, device=dev)
+        cdt = torch.uint8 if self.kv8 else dt
+        self.kc = torch.empty((nt, *cshape), dtype=cdt, device=dev)
         self.vc = torch.empty_like(self.kc)
+        if self.kv8:
+            self.ks = torch.empty((nt, *cshape[:-1]), dtype=torch.float32, device=dev)
+            self.vs = torch.empty_like(self.ks)
         qs = (nt, cfg.B, cfg.K, cfg.Hq, cfg.D)
         bs = (nt, cfg.B, cfg.K, cfg.Hkv, cfg.D)
         self.q = {v: torch.empty(qs, dtype=dt, device=dev) for v in ("diff", "ar")}
@@ -156,14 +168,23 @@ class Step:
         for l in range(nl):
             lay = st.layers[0] if l == 0 else W.layer_inputs(cfg, l, st.lens, st.num_pages,
                                                               st.capacity)
-            self.kc[l].copy_(lay.k_cache)
-            self.vc[l].copy_(lay.v_cache)
+            if self.kv8:
+                kc8, ks = W.fp8_cache(lay.k_cache, W.seed_of(cfg, W.T_FP8_KS, l))
+                vc8, vs = W.fp8_cache(lay.v_cache, W.seed_of(cfg, W.T_FP8_VS, l))
+                self.kc[l].copy_(kc8)
+                self.vc[l].copy_(vc8)
+                self.ks[l].copy_(ks)
+                self.vs[l].copy_(vs)
+            else:
+                self.kc[l].copy_(lay.k_cache)
+                self.vc[l].copy_(lay.v_cache)
             for v in ("diff", "ar"):
                 self.q[v][l].copy_(getattr(lay, f"q_{v}"))
                 self.kb[v][l].copy_(getattr(lay, f"k_blk_{v}"))
                 self.vb[v][l].copy_(getattr(lay, f"v_blk_{v}"))
-        for x in [self.kc, self.vc] + [d[v] for d in (self.q, self.kb, self.vb)
-                                       for v in ("diff", "ar")]:
+        scales = [self.ks, self.vs] if self.kv8 else []
+        for x in [self.kc, self.vc] + scales + [d[v] for d in (self.q, self.kb, self.vb)
+                                                for v in ("diff", "ar")]:
             for si in range(1, sets):   # copies: other addresses, same values
                 x[si * nl:(si + 1) * nl].copy_(x[:nl])
         log(f"inputs for {nl} layers x {sets} input sets generated in {time.time() - t0:.1f}s")
@@ -189,7 +210,9 @@ class Step:
             self.ar_logits.append(al.to(dev))
         lmax = int(st.lens.max())
         self.caches = [api.make_cache(self.kc[l], self.vc[l], self.lens,
-                                      page_table=self.page_table, max_len=lmax)
+                                      page_table=self.page_table, max_len=lmax,
+                                      k_scale=self.ks[l] if self.kv8 else None,
+                                      v_scale=self.vs[l] if self.kv8 else None)
                        for l in range(nt)]
         self.out = torch.empty(qs[1:], dtype=dt, device=dev)
         self.lse = torch.empty((cfg.B, cfg.Hq, cfg.K), dtype=torch.float32, device=dev)
@@ -236,7 +259,10 @@ class Step:
     def attn_bytes_per_launch(self):
         c = self.cfg
         e = 2 if c.dtype == "bf16" else 4
-        cache = int(self.step_inputs.lens.sum()) * c.Hkv * c.D * 2 * e
+        # K and V rows of the cache: D elements each (E4M3: one byte per code
+        # plus the row's fp32 scale)
+        row = c.D * 1 + 4 if self.kv8 else c.D * e
+        cache = int(self.step_inputs.lens.sum()) * c.Hkv * row * 2
         blk = c.B * c.K * (2 * c.Hq + 2 * c.Hkv) * c.D * e
         return cache + blk + c.B * c.Hq * c.K * 4
 
@@ -250,7 +276,8 @@ class Step:
         c = self.cfg
         e = 2 if c.dtype == "bf16" else 4
         logits = 2 * c.B * c.K * c.V * e
-        append = 2 * 2 * c.Hkv * c.D * e * n_mean_total * c.layers
+        row_out = c.D * 1 + 4 if self.kv8 else c.D * e
+        append = 2 * c.Hkv * (c.D * e + row_out) * n_mean_total * c.layers
         return 2 * c.layers * self.attn_bytes_per_launch() + logits + append
 
 
@@ -494,13 +521,16 @@ def main():
     if args.mdiff:
         mdiff_main(args)
         return
+    if args.decode_step:
+        decode_step_main(args)
+        return
     cfg = W.CONFIGS[args.config]
     if args.K:
         cfg = cfg.with_(K=args.K)
     splits = args.splits or cfg.num_splits
     log(f"workload {cfg.name} K={cfg.K} splits={splits or 'auto'}")
     calibrate(args.calib_bytes)
-    step = Step(cfg, splits, args.sets, args.draws)
+    step = Step(cfg, splits, args.sets, args.draws, kv=args.kv)
     graph = not args.no_graph
 
     ms_run, per_run = timed(step.run, args.steps, args.warmup, graph, args.repeats)
@@ -538,15 +568,17 @@ def main():
                    "K": cfg.K, "L": cfg.L if cfg.L_range is None else list(cfg.L_range),
                    "layers": cfg.layers, "V": cfg.V, "paged": cfg.paged,
                    "num_splits": splits or "auto", "graph": graph, "input_sets": step.sets,
-                   "logits_draws": step.draws},
+                   "logits_draws": step.draws, "kv_cache": args.kv},
         "timing": {"repeats": args.repeats, "statistic": "median",
                    "ms_per_step_repeats": [round(m / step.nsteps, 5) for m in per_run],
                    "us_per_attn_launch_repeats":
                        [round(m * 1e3 / (2 * cfg.layers * step.sets), 3) for m in per_attn]},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None if args.K else measured_traffic(cfg.name, args.splits),
-                     "kernel": "block attention (attn_bf16_kernel + split merge), per launch",
+                     "traffic": None if (args.K or step.kv8) else measured_traffic(cfg.name,
+                                                                                  args.splits),
+                     "kernel": "block attention (attn_bf16_kernel + split merge), per launch"
+                               + (", E4M3 cache" if step.kv8 else ""),
                      "us_per_launch": round(us_attn, 3), "bytes_per_launch": attn_b,
                      "mfma_frac": round(attn_f / (us_attn * 1e-6) / 2.5e15, 4)},
         "step_hbm_tbps": round(step.step_bytes(n_mean_total) / (ms_step * 1e-3) / 1e12, 3),
@@ -639,6 +671,57 @@ def mdiff_main(args):
                                "cpu_model": cpu_model(),
                                "sample": f"fp64 oracle on {len(sel)} of {Bn * NB} blocks "
                                          "(every 16th block of sequence 0), scaled by FLOPs"}
+    print(json.dumps(res), flush=True)
+
+
+def decode_step_main(args):
+    """One whole decode step of a 36-layer Qwen3-8B-shaped model with random
+    weights (drawn on the GPU, seeded), B = 1, K = 32, a synthetic 8,192-row
+    cache per layer: the diffusion pass (36 layers, bidirectional block), its
+    greedy candidates, the AR pass (36 layers, causal block), consensus, the
+    36-layer append.  Algorithmic bytes: every weight matrix each pass reads
+    (the views' own attention projections, the shared MLP, the LM head), the
+    caches twice, the block rows, and the append.  The weight-streaming
+    projections dominate."""
+    import torch
+    import workloads as W
+    from ar_shared_kv_amd.decode import DecodeModel, Dims
+    d = Dims(layers=36)
+    B, K, L = 1, 32, 8192
+    cap = L + K
+    t0 = time.time()
+    w = W.model_weights(d, seed=0, device="cuda")
+    gm = DecodeModel(d, w, B, K, cap)
+    g = torch.Generator(device="cuda").manual_seed(77)
+    gm.kc.copy_(torch.randn(gm.kc.shape, generator=g, device="cuda").to(torch.bfloat16))
+    gm.vc.copy_(torch.randn(gm.vc.shape, generator=g, device="cuda").to(torch.bfloat16))
+    gm.set_lengths(L)
+    gm.anchor.fill_(1234)
+    log(f"36-layer model and caches ready in {time.time() - t0:.1f}s")
+    step = lambda: gm.orthrus_step(advance=False)  # noqa: E731
+    ms, per = timed(step, args.steps, args.warmup, not args.no_graph, args.repeats)
+    nqkv = (d.Hq + 2 * d.Hkv) * d.D
+    layer_w = 2 * (nqkv * d.H + d.H * d.Hq * d.D + 2 * d.I * d.H + d.H * d.I)    # bytes, per view
+    kv_bytes = L * d.Hkv * d.D * 2 * 2                                          # one layer's cache
+    blk = B * K * (2 * d.Hq + 2 * d.Hkv) * d.D * 2                              # q, o, block K/V
+    step_bytes = 2 * (d.layers * (layer_w + kv_bytes + blk) + 2 * d.V * d.H) \
+        + d.layers * 2 * d.Hkv * d.D * 2 * 2 * B                                 # + the append
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "Orthrus decode steps/s, whole model (36-layer Qwen3-8B shape, random weights)",
+        "value": round(1e3 / ms, 3), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3-8b-36layers-decode-step", "B": B, "K": K, "L": L,
+                   "layers": d.layers, "H": d.H, "I": d.I, "V": d.V, "graph": not args.no_graph},
+        "timing": {"repeats": args.repeats, "statistic": "median",
+                   "ms_repeats": [round(m, 5) for m in per]},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "whole step (weight-streaming projections dominate)",
+                     "bytes_per_step": step_bytes},
+        "accepted_n": gm.n_emit.cpu().tolist(),
+    }
     print(json.dumps(res), flush=True)
 
 

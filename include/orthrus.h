@@ -53,7 +53,7 @@ typedef enum {
     ORTHRUS_ERR_LAUNCH = 6       /* the HIP runtime reported an error      */
 } orthrus_status;
 
-typedef enum { ORTHRUS_F32 = 0, ORTHRUS_BF16 = 1 } orthrus_dtype;
+typedef enum { ORTHRUS_F32 = 0, ORTHRUS_BF16 = 1, ORTHRUS_FP8_E4M3 = 2 } orthrus_dtype;
 
 /* In-block visibility of the block rows:
  *   BIDIR  -- every block row sees every block row (the diffusion view's
@@ -79,10 +79,23 @@ typedef enum { ORTHRUS_LAYOUT_CONTIGUOUS = 0, ORTHRUS_LAYOUT_PAGED = 1 } orthrus
  *  max_len   host-side upper bound on lens[b] used to size the split-KV grid
  *            (0 = derive it from capacity or max_pages_per_req*page_size).
  *            A wrong hint costs speed, never correctness.
+ *  kv_dtype  element type of k and v: 0 (the call's dtype) or ORTHRUS_FP8_E4M3.
+ *            FP8_E4M3 (bf16 calls, D = 128): k and v hold OCP FP8 E4M3 codes
+ *            (1 byte per element: sign, 4 exponent bits with bias 7, 3
+ *            mantissa bits; no infinities; S.1111.111 is NaN; largest finite
+ *            448) laid out as above, and k_scale / v_scale hold one fp32 scale
+ *            per cache row and KV head, laid out like the rows without D
+ *            ([B][Hkv][capacity], or [num_pages][Hkv][page_size]).  A row's
+ *            values are code * scale.  Scales are powers of two (so that
+ *            code * scale is exact in bf16); orthrus_kv_append writes
+ *            2^e with e the smallest integer such that 448 * 2^e >= the
+ *            row's largest |value| (e >= -120; an all-zero row gets 1).
+ *            This is the "low-precision kernels" direction of the
+ *            agents-report outlook: the cache streams half the bytes.
  * Caller contracts (not checked on the device): 0 <= lens[b]; for
  * CONTIGUOUS lens[b] <= capacity; for PAGED every page id the rows
  * 0..lens[b]-1 (and, for an append, the appended rows) map to is in
- * [0, num_pages).
+ * [0, num_pages); FP8 scales are finite powers of two.
  */
 typedef struct orthrus_cache {
     int32_t layout;              /* orthrus_layout                          */
@@ -95,6 +108,10 @@ typedef struct orthrus_cache {
     int64_t max_pages_per_req;   /* PAGED                                   */
     const int32_t *lens;         /* device int32 [B]                        */
     int64_t max_len;             /* host hint, see above                    */
+    int32_t kv_dtype;            /* 0 or ORTHRUS_FP8_E4M3                   */
+    int32_t reserved;            /* 0                                       */
+    float *k_scale;              /* FP8: device fp32 scale per row and head */
+    float *v_scale;              /* FP8: device fp32 scale per row and head */
 } orthrus_cache;
 
 /*
@@ -232,6 +249,17 @@ int orthrus_consensus(const void *diff_logits, const void *ar_logits, int B,
 size_t orthrus_consensus_workspace_bytes(int B, int K, int V, int dtype);
 
 /*
+ * orthrus_consensus_tokens -- the consensus of orthrus_consensus from the two
+ * views' greedy tokens themselves (e.g. from orthrus_lmhead_argmax, which
+ * never writes logits): diff_tok, ar_tok device int32 [B][K] (read only);
+ * the other outputs and limits as in orthrus_consensus.  No workspace.
+ */
+int orthrus_consensus_tokens(const int32_t *diff_tok, const int32_t *ar_tok,
+                             int B, int K, int32_t *n_match, int32_t *n_emit,
+                             int32_t *emit_off, int32_t *emitted,
+                             int32_t *next_anchor, hipStream_t stream);
+
+/*
  * orthrus_argmax -- the greedy-prediction half of orthrus_consensus on its
  * own (a pipeline needs the diffusion view's candidates before the AR pass;
  * summary §2.3 steps 1-2): idx[r] = argmax_v logits[r][v], lowest index on
@@ -285,7 +313,11 @@ size_t orthrus_lmhead_argmax_workspace_bytes(int R, int H, int V, int dtype);
  *
  *  cache     layer 0's cache; layer l's k/v are at cache->k/v + l *
  *            cache_layer_stride ELEMENTS (paged: one page table for all
- *            layers).  cache->lens is read, never written.
+ *            layers).  cache->lens is read, never written.  An FP8_E4M3
+ *            cache (bf16 rows, D = 128) quantizes each appended row and head:
+ *            scale 2^e as described at orthrus_cache, code = value / 2^e
+ *            rounded to nearest even; layer l's scales are at k_scale /
+ *            v_scale + l * cache_layer_stride / D (the stride counts codes).
  *  k_blk, v_blk  layer 0's AR-view block rows [B][K][Hkv][D]; layer l at
  *            + l * blk_layer_stride elements
  *  n_emit    device int32 [B], each in 0..K (e.g. orthrus_consensus output)
@@ -315,6 +347,70 @@ int orthrus_kv_append(const orthrus_cache *cache, const void *k_blk,
  */
 int orthrus_stream_read(const void *src, size_t bytes, int work_groups,
                         uint32_t *sink, hipStream_t stream);
+
+/*
+ * The decode step around the Orthrus kernels (summary §2.3 steps 1-2: the
+ * diffusion view projects K candidates in one forward pass over its block,
+ * the frozen AR view verifies the block in one forward pass; each pass runs
+ * the model's layers on the block's B*K rows).  A Qwen3-style layer:
+ *   x = rmsnorm(h) -> qkv = x Wqkv^T -> q, k = rmsnorm_head(q, k) then rotary
+ *   embedding, v copied -> o = block attention -> h += o Wo^T ->
+ *   x = rmsnorm(h) -> h += swiglu(x Wgu^T) Wdown^T
+ * with an fp32 residual stream h and bf16 weights and projection inputs.
+ * The views differ only in their attention weights (the diffusion module's
+ * own Wqkv, Wo) and the block mask.  Rows are [R][...] row-major.
+ */
+
+/*
+ * orthrus_gemm -- y = x W^T (+ residual): x bf16 [R][Kin], W bf16 [N][Kin]
+ * (a linear layer's weight, one row per output), residual fp32 [R][N] or
+ * NULL, y [R][N] in out_dtype (F32 or BF16; y may be the residual itself).
+ * fp32 accumulation in a fixed order per output that does not depend on R
+ * (the input dimension is split S ways by N and Kin only; the partial sums
+ * are added in split order).  Kin a multiple of 64, N a multiple of 4,
+ * pointers 16-byte aligned.  workspace >= orthrus_gemm_workspace_bytes.
+ */
+int orthrus_gemm(const void *x, const void *w, const float *residual, void *y,
+                 int R, int N, int Kin, int out_dtype, void *workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+size_t orthrus_gemm_workspace_bytes(int R, int N, int Kin);
+
+/* orthrus_rmsnorm -- y[r] = x[r] / sqrt(mean_k x[r][k]^2 + eps) * weight:
+ * x fp32 [R][H], weight bf16 [H], y bf16 [R][H]. */
+int orthrus_rmsnorm(const float *x, const void *weight, void *y, int R, int H,
+                    float eps, hipStream_t stream);
+
+/* orthrus_qk_norm_rope -- from the fp32 projection qkv [R][(Hq+2Hkv)*D]
+ * (q heads, then k heads, then v heads) of a block's rows (row r is block
+ * row r % K of request r / K, at position lens[r / K] + r % K; lens device
+ * int32): q and k heads are normalised by RMSNorm over D (weights q_norm,
+ * k_norm bf16 [D]) and rotated by the rotary embedding (pairs (d, d + D/2),
+ * angle position * rope_theta^(-2d/D), computed in fp64); v is copied.
+ * Outputs bf16 q [R][Hq][D], k [R][Hkv][D], v [R][Hkv][D] -- the block
+ * attention's q, k_blk, v_blk.  D = 128, R a multiple of K. */
+int orthrus_qk_norm_rope(const float *qkv, const void *q_norm,
+                         const void *k_norm, const int32_t *lens, int K,
+                         void *q, void *k, void *v, int R, int Hq, int Hkv,
+                         int D, float eps, float rope_theta, hipStream_t stream);
+
+/* orthrus_block_tokens -- a view's block input tokens: out[b][0] = anchor[b]
+ * and out[b][i] = cand[b][i-1] for i >= 1 (the AR view: anchor, then the
+ * first K-1 candidates), or = fill when cand is NULL (the diffusion view:
+ * anchor, then <mask>).  Device int32: anchor [B], cand [B][K], out [B][K]. */
+int orthrus_block_tokens(const int32_t *anchor, const int32_t *cand,
+                         int32_t fill, int32_t *out, int B, int K,
+                         hipStream_t stream);
+
+/* orthrus_swiglu -- act[r][i] = silu(gate_up[r][i]) * gate_up[r][I + i],
+ * silu(g) = g / (1 + e^-g): gate_up fp32 [R][2I], act bf16 [R][I]. */
+int orthrus_swiglu(const float *gate_up, void *act, int R, int I,
+                   hipStream_t stream);
+
+/* orthrus_embed -- h[r] = table[tokens[r]] (bf16 -> fp32): tokens device int32
+ * [R] (caller contract: valid rows of table), table bf16 [rows][H], h fp32
+ * [R][H]. */
+int orthrus_embed(const int32_t *tokens, const void *table, float *h, int R,
+                  int H, hipStream_t stream);
 
 /* Static string naming a status code ("ok", "null pointer", ...). */
 const char *orthrus_status_string(int status);

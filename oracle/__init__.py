@@ -21,6 +21,12 @@ of the pages it follows (see the C file's header for the source list):
 * ``consensus``   -- left-to-right exact consensus; summary §2.3 step 3.
 * ``kv_append``   -- commit of the accepted rows' KV; summary §2.3 step 3 and
   the agents-report core-design section.
+* ``e4m3_decode`` / ``e4m3_encode`` / ``fp8_scale_exp`` / ``dequant_fp8`` /
+  ``kv_append_fp8`` -- the FP8 (OCP E4M3) KV cache: decoding and
+  round-to-nearest-even encoding from the format's definition, the per-row
+  power-of-two scale, and the quantizing commit; the agents-report outlook
+  (low-precision kernels).  Attention over an FP8 cache is ``block_attn``
+  on the dequantized values.
 
 Parity pins: every function is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_*.py`` (library routines, closed forms, invariants and
@@ -73,6 +79,17 @@ def _load():
             lib.oracle_kv_append.restype = I
             lib.oracle_mdiff_attn.argtypes = [P, P, P, L, P, P, P, I, I, I, I, I, I, D, P, P]
             lib.oracle_mdiff_attn.restype = I
+            lib.oracle_e4m3_decode.argtypes = [I]
+            lib.oracle_e4m3_decode.restype = D
+            lib.oracle_e4m3_encode.argtypes = [D]
+            lib.oracle_e4m3_encode.restype = I
+            lib.oracle_fp8_scale_exp.argtypes = [D]
+            lib.oracle_fp8_scale_exp.restype = I
+            lib.oracle_e4m3_decode_array.argtypes = [P, L, P]
+            lib.oracle_e4m3_decode_array.restype = None
+            lib.oracle_kv_append_fp8.argtypes = [P, P, P, P, I, L, I, P, I, I, P, P, P, P, P,
+                                                 I, I, I, I, I, L, L]
+            lib.oracle_kv_append_fp8.restype = I
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = I
             lib.oracle_set_num_threads.argtypes = [I]
@@ -181,6 +198,62 @@ def lmhead_logits(hidden, weight, chunk: int = 8192):
 def lmhead_argmax(hidden, weight):
     """Greedy tokens: argmax_v of the fp64 logits, lowest index on ties."""
     return argmax_rows(lmhead_logits(hidden, weight))
+
+
+def e4m3_decode(code: int) -> float:
+    """Value of one OCP FP8 E4M3 code (NaN for S.1111.111)."""
+    return float(_load().oracle_e4m3_decode(int(code)))
+
+
+def e4m3_encode(x: float) -> int:
+    """Nearest E4M3 code to x, ties to even; raises beyond +-448."""
+    c = _load().oracle_e4m3_encode(float(x))
+    if c < 0:
+        raise ValueError(f"{x} is outside the E4M3 range")
+    return c
+
+
+def fp8_scale_exp(amax: float) -> int:
+    """Smallest e >= -120 with 448 * 2^e >= amax (0 for amax = 0)."""
+    return int(_load().oracle_fp8_scale_exp(float(amax)))
+
+
+def dequant_fp8(codes, scales):
+    """fp64 values of an E4M3 cache: decode(codes) * scale of the row.  codes
+    [..., D] uint8, scales [...] float32 (one per row)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e4m3_decode_array(_ptr(c), c.size, _ptr(out))
+    return out * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def kv_append_fp8(k_codes, v_codes, k_scale, v_scale, k_blk, v_blk, n, lens, *,
+                  layout=CONTIGUOUS, page_table=None):
+    """Append accepted AR rows into copies of an E4M3 cache, quantizing each
+    (row, KV head): k_codes/v_codes [layers, ...cache layout...] uint8,
+    k_scale/v_scale [layers, ...rows...] float32, k_blk/v_blk [layers, B, K,
+    Hkv, D] (any real type; converted to fp64 exactly).  Returns (k_codes',
+    v_codes', k_scale', v_scale', lens_out)."""
+    kc = np.array(k_codes, dtype=np.uint8, copy=True, order="C")
+    vc = np.array(v_codes, dtype=np.uint8, copy=True, order="C")
+    ks = np.array(k_scale, dtype=np.float32, copy=True, order="C")
+    vs = np.array(v_scale, dtype=np.float32, copy=True, order="C")
+    kb, vb = _f64(k_blk), _f64(v_blk)
+    layers, B, K, Hkv, D = kb.shape
+    n, lens = _i32(n), _i32(lens)
+    if layout == CONTIGUOUS:
+        cap, page_size, num_pages, max_pages, pt = kc.shape[3], 16, 0, 0, None
+    else:
+        pt = _i32(page_table)
+        cap, num_pages, page_size, max_pages = 0, kc.shape[1], kc.shape[3], pt.shape[1]
+    lens_out = np.empty(B, np.int32)
+    rc = _load().oracle_kv_append_fp8(_ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs), layout, cap,
+                                      page_size, _ptr(pt), max_pages, num_pages, _ptr(lens),
+                                      _ptr(kb), _ptr(vb), _ptr(n), _ptr(lens_out), B, K, Hkv, D,
+                                      layers, kc[0].size, kb[0].size)
+    if rc != 0:
+        raise ValueError("oracle_kv_append_fp8 rejected its arguments")
+    return kc, vc, ks, vs, lens_out
 
 
 def consensus(d_tok, a_tok):

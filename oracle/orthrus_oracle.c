@@ -333,3 +333,141 @@ int oracle_mdiff_attn(const double *q, const double *k_ctx, const double *v_ctx,
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * FP8 KV cache (the agents-report outlook names low-precision kernels as the
+ * direction; the format is the OCP 8-bit floating point E4M3 of the OCP
+ * "OFP8" specification): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits.  Exponent field 0 holds the subnormals m * 2^-9 (m = 0..7); fields
+ * 1..15 hold (1 + m/8) * 2^(field-7); the code S.1111.111 is NaN and there
+ * are no infinities, so the largest finite magnitude is 1.75 * 2^8 = 448.
+ */
+
+/* Value of one code (NaN for S.1111.111). */
+double oracle_e4m3_decode(int code)
+{
+    const int sign = (code >> 7) & 1;
+    const int field = (code >> 3) & 15;
+    const int m = code & 7;
+    double v;
+    if (field == 15 && m == 7) return NAN;
+    if (field == 0) v = ldexp((double)m, -9);
+    else v = ldexp(1.0 + m / 8.0, field - 7);
+    return sign ? -v : v;
+}
+
+/* Nearest code to x, ties to the even code (the one whose mantissa is even);
+ * |x| must not exceed 448.  Returns -1 otherwise. */
+int oracle_e4m3_encode(double x)
+{
+    if (isnan(x) || fabs(x) > 448.0) return -1;
+    const int sign = signbit(x) ? 1 : 0;
+    double a = fabs(x);
+    /* candidates: the representable magnitudes are k * 2^(E-3) on the
+     * binade [2^E, 2^(E+1)) for E >= -6, and k * 2^-9 below 2^-6 */
+    int field;
+    double step;
+    if (a < ldexp(1.0, -6)) {
+        field = 0;
+        step = ldexp(1.0, -9);
+    } else {
+        int E;
+        frexp(a, &E);          /* a = f * 2^E, f in [0.5, 1): binade [2^(E-1), 2^E) */
+        E -= 1;
+        field = E + 7;
+        step = ldexp(1.0, E - 3);
+    }
+    double q = a / step;       /* exact: a and step are dyadic */
+    double lo = floor(q);
+    double r = q - lo;
+    double k = (r > 0.5 || (r == 0.5 && fmod(lo, 2.0) != 0.0)) ? lo + 1.0 : lo;
+    /* k counts steps of this binade: field 0 codes k = 0..8 (8 = 2^-6, the
+     * smallest normal, whose code is 0.0001.000 = 8); normal binades k =
+     * 8..16 (16 = the next binade's 1.000) */
+    int code;
+    if (field == 0) {
+        code = (int)k;
+    } else {
+        int m = (int)k - 8;
+        int f = field;
+        if (m == 8) { m = 0; f += 1; }
+        code = (f << 3) | m;
+    }
+    if (code > 0x7e) return -1;           /* beyond 448 */
+    return (sign << 7) | code;
+}
+
+/* Scale exponent of a row whose largest magnitude is amax: the smallest
+ * integer e >= -120 with 448 * 2^e >= amax (so every value / 2^e fits the
+ * format); 0 for amax = 0.  Written as the search it defines. */
+int oracle_fp8_scale_exp(double amax)
+{
+    if (amax == 0.0) return 0;
+    int e = -120;
+    while (448.0 * ldexp(1.0, e) < amax) ++e;
+    return e;
+}
+
+/*
+ * Commit into an FP8 cache: the accepted AR rows of oracle_kv_append, each
+ * (row, KV head) of D values quantized on the way.  Scale s = 2^e with
+ * e = oracle_fp8_scale_exp(max |value|); code = encode(value / s).  Codes go
+ * where oracle_kv_append puts elements (one byte each); the scale goes to
+ * the same row index of k_scale / v_scale (the row layout without D).
+ * k_blk/v_blk are fp64 values (exact copies of the bf16 rows).  Returns -1 on
+ * a bad argument or page.
+ */
+int oracle_kv_append_fp8(unsigned char *k_cache, unsigned char *v_cache, float *k_scale,
+                         float *v_scale, int layout, long cap, int page_size,
+                         const int32_t *page_table, int max_pages, int num_pages,
+                         const int32_t *lens, const double *k_blk, const double *v_blk,
+                         const int32_t *n, int32_t *lens_out, int B, int K, int Hkv, int D,
+                         int layers, long cache_layer_stride, long blk_layer_stride)
+{
+    for (int b = 0; b < B; ++b)
+        if (n[b] < 0 || n[b] > K) return -1;
+    for (int l = 0; l < layers; ++l) {
+        for (int b = 0; b < B; ++b) {
+            for (int i = 0; i < n[b]; ++i) {
+                long t = (long)lens[b] + i;
+                for (int g = 0; g < Hkv; ++g) {
+                    long dst;
+                    if (layout == O_CONTIGUOUS) {
+                        if (t >= cap) return -1;
+                        dst = ((long)b * Hkv + g) * cap + t;
+                    } else {
+                        long lp = t / page_size;
+                        if (lp >= max_pages) return -1;
+                        int32_t page = page_table[(long)b * max_pages + lp];
+                        if (page < 0 || page >= num_pages) return -1;
+                        dst = ((long)page * Hkv + g) * page_size + t % page_size;
+                    }
+                    for (int which = 0; which < 2; ++which) {
+                        const double *src = (which ? v_blk : k_blk) + l * blk_layer_stride +
+                                            (((long)b * K + i) * Hkv + g) * D;
+                        unsigned char *cc = (which ? v_cache : k_cache) + l * cache_layer_stride;
+                        float *sc = (which ? v_scale : k_scale) + l * (cache_layer_stride / D);
+                        double amax = 0.0;
+                        for (int d = 0; d < D; ++d)
+                            if (fabs(src[d]) > amax) amax = fabs(src[d]);
+                        const int e = oracle_fp8_scale_exp(amax);
+                        for (int d = 0; d < D; ++d) {
+                            const int code = oracle_e4m3_encode(ldexp(src[d], -e));
+                            if (code < 0) return -1;
+                            cc[dst * D + d] = (unsigned char)code;
+                        }
+                        sc[dst] = (float)ldexp(1.0, e);
+                    }
+                }
+            }
+        }
+    }
+    for (int b = 0; b < B; ++b) lens_out[b] = lens[b] + n[b];
+    return 0;
+}
+
+/* oracle_e4m3_decode over an array. */
+void oracle_e4m3_decode_array(const unsigned char *codes, long n, double *out)
+{
+    for (long i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(codes[i]);
+}

@@ -310,3 +310,59 @@ def mdiff_inputs(B: int, N: int, K: int, Hq: int, Hkv: int, D: int, layout: str 
         k_ctx=normal((B, Hkv, N, D), dt, s(T_MD_KC)),
         v_ctx=normal((B, Hkv, N, D), dt, s(T_MD_VC)),
         anchors=mdiff_anchors(B, N, K, NB, layout, s(T_MD_ANCH)))
+
+
+T_FP8_KS, T_FP8_VS = 21, 22
+
+
+def fp8_cache(values: torch.Tensor, seed: int):
+    """An OCP E4M3 cache holding about `values`: each row (the last axis) gets
+    a random power-of-two scale 2^e, e uniform in {-7, -6, -5}, and codes =
+    the E4M3 nearest to value / 2^e (clamped to +-448).  The scales are drawn,
+    not derived from the rows, so this is input construction, not the
+    quantizer the append uses.  Returns (codes uint8 [..., D], scales float32
+    [...])."""
+    e = torch.randint(-7, -4, values.shape[:-1], generator=gen(seed)).to(torch.float32)
+    sc = torch.exp2(e)
+    x = (values.float() / sc[..., None]).clamp(-448.0, 448.0)
+    codes = x.to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), sc.contiguous()
+
+
+T_MODEL = 30
+
+
+def model_weights(dims, seed: int = 0, device="cpu"):
+    """Random weights of a Qwen3-style model (the layer of the decode step,
+    see oracle.model) at the given dimensions, bf16, seeded.  Scales keep
+    activations O(1): projections N(0, 1/fan_in), norm weights 1 + N(0,
+    0.1^2), embeddings N(0, 1).  The diffusion view's attention weights start
+    from the AR ones (the agents-report core design: the module is
+    initialised from its AR counterparts) plus an independent N(0, 0.2^2 /
+    fan_in) change, standing in for its training.  The embedding table has
+    one extra row, index V: the <mask> token.  device="cuda" draws on the GPU
+    (seeded, for the benchmark's 36-layer model only)."""
+    g = torch.Generator(device=device).manual_seed(1000 * 96 + T_MODEL + 100000 * seed)
+
+    def rn(shape, std, mean=0.0):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        return (x * std + mean).to(torch.bfloat16)
+
+    H, Hq, Hkv, D, I, V = dims.H, dims.Hq, dims.Hkv, dims.D, dims.I, dims.V
+    nqkv = (Hq + 2 * Hkv) * D
+    w = {"embed": rn((V + 1, H), 1.0), "final_norm": rn((H,), 0.1, 1.0),
+         "lm_head": rn((V, H), H ** -0.5)}
+    for l in range(dims.layers):
+        w[f"l{l}.in_norm"] = rn((H,), 0.1, 1.0)
+        w[f"l{l}.post_norm"] = rn((H,), 0.1, 1.0)
+        w[f"l{l}.q_norm"] = rn((D,), 0.1, 1.0)
+        w[f"l{l}.k_norm"] = rn((D,), 0.1, 1.0)
+        w[f"l{l}.ar.wqkv"] = rn((nqkv, H), H ** -0.5)
+        w[f"l{l}.ar.wo"] = rn((H, Hq * D), (Hq * D) ** -0.5)
+        w[f"l{l}.diff.wqkv"] = (w[f"l{l}.ar.wqkv"].float()
+                                + rn((nqkv, H), 0.2 * H ** -0.5).float()).to(torch.bfloat16)
+        w[f"l{l}.diff.wo"] = (w[f"l{l}.ar.wo"].float()
+                              + rn((H, Hq * D), 0.2 * (Hq * D) ** -0.5).float()).to(torch.bfloat16)
+        w[f"l{l}.wgu"] = rn((2 * I, H), H ** -0.5)
+        w[f"l{l}.wdown"] = rn((H, I), I ** -0.5)
+    return w

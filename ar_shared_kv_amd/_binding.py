@@ -79,6 +79,11 @@ SIGNATURES = {
     "orthrus_gemm": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
     "orthrus_gemm_workspace_bytes": (_SZ, [_I, _I, _I]),
     "orthrus_rmsnorm": (_I, [_P, _P, _P, _I, _I, _F, _P]),
+    "orthrus_gemm_epilogue_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "orthrus_gemm_rmsnorm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _SZ, _P]),
+    "orthrus_gemm_swiglu": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "orthrus_gemm_qk_norm_rope": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I,
+                                       _F, _F, _P, _SZ, _P]),
     "orthrus_qk_norm_rope": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _F, _P]),
     "orthrus_block_tokens": (_I, [_P, _P, _I, _P, _I, _I, _P]),
     "orthrus_swiglu": (_I, [_P, _P, _I, _I, _P]),
@@ -289,6 +294,30 @@ def orthrus_qk_norm_rope(qkv, q_norm, k_norm, lens, K, q, k, v, R, Hq, Hkv, D, e
 
 def orthrus_block_tokens(anchor, cand, fill, out, B, K, stream=None) -> int:
     return lib().orthrus_block_tokens(ptr(anchor), ptr(cand), fill, ptr(out), B, K, _st(stream))
+
+
+def orthrus_gemm_epilogue_workspace_bytes(R, N, Kin) -> int:
+    return lib().orthrus_gemm_epilogue_workspace_bytes(R, N, Kin)
+
+
+def orthrus_gemm_rmsnorm(x, w, h, norm_weight, xn, R, H, Kin, eps, workspace, workspace_bytes,
+                         stream=None) -> int:
+    return lib().orthrus_gemm_rmsnorm(ptr(x), ptr(w), ptr(h), ptr(norm_weight), ptr(xn), R, H,
+                                      Kin, eps, ptr(workspace), workspace_bytes, _st(stream))
+
+
+def orthrus_gemm_swiglu(x, w_gate_up, act, R, I, Kin, workspace, workspace_bytes,
+                        stream=None) -> int:
+    return lib().orthrus_gemm_swiglu(ptr(x), ptr(w_gate_up), ptr(act), R, I, Kin, ptr(workspace),
+                                     workspace_bytes, _st(stream))
+
+
+def orthrus_gemm_qk_norm_rope(x, w_qkv, q_norm, k_norm, lens, K, q, k, v, R, Hq, Hkv, D, Kin,
+                              eps, theta, workspace, workspace_bytes, stream=None) -> int:
+    return lib().orthrus_gemm_qk_norm_rope(ptr(x), ptr(w_qkv), ptr(q_norm), ptr(k_norm),
+                                           ptr(lens), K, ptr(q), ptr(k), ptr(v), R, Hq, Hkv, D,
+                                           Kin, eps, theta, ptr(workspace), workspace_bytes,
+                                           _st(stream))
 
 
 def orthrus_swiglu(gate_up, act, R, I, stream=None) -> int:

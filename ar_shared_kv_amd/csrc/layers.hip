@@ -150,15 +150,27 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int 
     }
 }
 
-// y = (res +) sum over s = 0..S-1 of part[s], in that order; fp32 or bf16.
+// The partial sums of the split input dimension are always added in split
+// order, v = ((p0 + p1) + p2) + ..., and a residual last (res + v), by every
+// kernel below that reads them: a fused epilogue gives the same bits as the
+// plain reduction followed by the separate kernel.
+__device__ __forceinline__ f32x4 sum_splits(const float* __restrict__ part, int S, int64_t stride,
+                                            int64_t i)
+{
+    f32x4 v = *(const f32x4*)(part + i);
+#pragma unroll 8
+    for (int s = 1; s < S; ++s) v += *(const f32x4*)(part + (int64_t)s * stride + i);
+    return v;
+}
+
+// y = (res +) sum of the S partials; fp32 or bf16.
 __global__ void __launch_bounds__(256)
 gemm_reduce_kernel(const float* __restrict__ part, int S, int64_t RN4, int out_bf16,
                    void* __restrict__ y, const float* __restrict__ res)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= RN4) return;
-    f32x4 v = ((const f32x4*)part)[i];
-    for (int s = 1; s < S; ++s) v += ((const f32x4*)part)[(int64_t)s * RN4 + i];
+    f32x4 v = sum_splits(part, S, RN4 * 4, i * 4);
     if (res) v = ((const f32x4*)res)[i] + v;
     if (out_bf16) ((u32x2*)y)[i] = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     else ((f32x4*)y)[i] = v;
@@ -175,28 +187,95 @@ int gemm_splits(int N, int Kin)
 }
 
 // ---------------------------------------------------------------- RMSNorm
-// y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * w, one work-group per row; the sum
-// of squares is reduced in a fixed order (per-thread runs, then lanes, then
-// waves), so a row's result does not depend on the other rows.
-__global__ void __launch_bounds__(256)
+// y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * w.  One work-group of 1024
+// threads per row; thread t holds the float4 groups t, t + 1024, ... (NG of
+// them) in registers.  The sum of squares has one fixed order: each thread
+// over its groups and their four values in turn, then the 64 lanes of a wave
+// (xor butterfly: every lane ends with the same bits), then the 16 waves in
+// index order.  So a row's result depends neither on R nor on which kernel
+// (the plain norm or a projection's fused epilogue) formed its input.
+constexpr int kNormThreads = 1024;
+constexpr int kNormMaxGroups = 4;             // H <= 4 * 4 * 1024
+
+template <int NG>
+__device__ __forceinline__ void rmsnorm_row(const f32x4 (&v)[NG], int H, const uint16_t* __restrict__ w,
+                                            uint16_t* __restrict__ yr, float eps)
+{
+    __shared__ float red[kNormThreads / 64];
+    const int tid = threadIdx.x;
+    const int H4 = H / 4;
+    float ss = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        if (tid + g * kNormThreads < H4) {
+            ss += v[g][0] * v[g][0];
+            ss += v[g][1] * v[g][1];
+            ss += v[g][2] * v[g][2];
+            ss += v[g][3] * v[g][3];
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = red[0];
+#pragma unroll
+    for (int i = 1; i < kNormThreads / 64; ++i) tot += red[i];
+    const float inv = 1.f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int j = tid + g * kNormThreads;
+        if (j < H4) {
+            const u32x2 wb = *(const u32x2*)(w + 4 * j);
+            const float y0 = v[g][0] * inv * bf16_bits_to_f32((uint16_t)(wb[0] & 0xffffu));
+            const float y1 = v[g][1] * inv * bf16_bits_to_f32((uint16_t)(wb[0] >> 16));
+            const float y2 = v[g][2] * inv * bf16_bits_to_f32((uint16_t)(wb[1] & 0xffffu));
+            const float y3 = v[g][3] * inv * bf16_bits_to_f32((uint16_t)(wb[1] >> 16));
+            *(u32x2*)(yr + 4 * j) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+        }
+    }
+}
+
+template <int NG>
+__global__ void __launch_bounds__(kNormThreads)
 rmsnorm_kernel(const float* __restrict__ x, const uint16_t* __restrict__ w, uint16_t* __restrict__ y,
                int H, float eps)
 {
-    const float* xr = x + (int64_t)blockIdx.x * H;
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += 256) ss += xr[i] * xr[i];
+    const int64_t row = blockIdx.x;
+    const float* xr = x + row * H;
+    f32x4 v[NG];
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-    __shared__ float part[4];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float tot = ((part[0] + part[1]) + part[2]) + part[3];
-    const float inv = 1.f / sqrtf(tot / (float)H + eps);
-    uint16_t* yr = y + (int64_t)blockIdx.x * H;
-    for (int i = threadIdx.x; i < H; i += 256) {
-        const float v = xr[i] * inv * bf16_bits_to_f32(w[i]);
-        yr[i] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
+    for (int g = 0; g < NG; ++g) {
+        const int j = threadIdx.x + g * kNormThreads;
+        v[g] = j < H / 4 ? *(const f32x4*)(xr + 4 * j) : f32x4{};
     }
+    rmsnorm_row<NG>(v, H, w, y + row * H, eps);
+}
+
+// The output (or down) projection's epilogue: h = res + sum of the partials
+// (stored, fp32), then the RMSNorm of h into y.  Bit for bit the plain
+// reduction followed by rmsnorm_kernel.
+template <int NG>
+__global__ void __launch_bounds__(kNormThreads)
+reduce_rmsnorm_kernel(const float* __restrict__ part, int S, int64_t RN, const float* res,
+                      float* h, const uint16_t* __restrict__ w, uint16_t* __restrict__ y, int H,
+                      float eps)
+{
+    const int64_t row = blockIdx.x;
+    f32x4 v[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int j = threadIdx.x + g * kNormThreads;
+        if (j < H / 4) {
+            const int64_t i = row * H + 4 * j;
+            v[g] = sum_splits(part, S, RN, i);
+            if (res) v[g] = *(const f32x4*)(res + i) + v[g];
+            *(f32x4*)(h + i) = v[g];
+        } else {
+            v[g] = f32x4{};
+        }
+    }
+    rmsnorm_row<NG>(v, H, w, y + row * H, eps);
 }
 
 // ------------------------------------------------------ QK norm + rotary
@@ -206,21 +285,16 @@ rmsnorm_kernel(const float* __restrict__ x, const uint16_t* __restrict__ w, uint
 // embedding with pairs (d, d + D/2) rotated by pos * theta^(-2d/D); v heads
 // are copied.  One wave per (row, head), D = 128 (lane l holds d = l and
 // l + 64).  Angles in fp64.
-__global__ void __launch_bounds__(256)
-qk_norm_rope_kernel(const float* __restrict__ qkv, const uint16_t* __restrict__ wq,
-                    const uint16_t* __restrict__ wk, const int32_t* __restrict__ lens, int K,
-                    uint16_t* __restrict__ q, uint16_t* __restrict__ k, uint16_t* __restrict__ v,
-                    int R, int Hq, int Hkv, float eps, double log_theta)
+__device__ __forceinline__ void qk_norm_rope_item(float x0, float x1, int r, int h, int lane,
+                                                  const uint16_t* __restrict__ wq,
+                                                  const uint16_t* __restrict__ wk,
+                                                  const int32_t* __restrict__ lens, int K,
+                                                  uint16_t* __restrict__ q,
+                                                  uint16_t* __restrict__ k,
+                                                  uint16_t* __restrict__ v, int Hq, int Hkv,
+                                                  float eps, double log_theta)
 {
     constexpr int D = 128;
-    const int heads = Hq + 2 * Hkv;
-    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= R * heads) return;
-    const int lane = threadIdx.x & 63;
-    const int r = item / heads;
-    const int h = item % heads;
-    const float* src = qkv + (int64_t)r * heads * D + (int64_t)h * D;
-    float x0 = src[lane], x1 = src[lane + 64];
     if (h >= Hq + Hkv) {                              // v: a copy
         uint16_t* dst = v + ((int64_t)r * Hkv + (h - Hq - Hkv)) * D;
         dst[lane] = (uint16_t)(pack_bf16x2(x0, 0.f) & 0xffffu);
@@ -246,19 +320,52 @@ qk_norm_rope_kernel(const float* __restrict__ qkv, const uint16_t* __restrict__ 
     dst[lane + 64] = (uint16_t)(pack_bf16x2(o1, 0.f) & 0xffffu);
 }
 
-// ---------------------------------------------------------------- SwiGLU
-// act[r][i] = silu(gu[r][i]) * gu[r][I + i], silu(g) = g / (1 + e^-g).
+// qkv holds S >= 1 partial sums [S][R][heads*D] of the projection (S = 1:
+// the projection itself), added in split order first.
 __global__ void __launch_bounds__(256)
-swiglu_kernel(const float* __restrict__ gu, uint16_t* __restrict__ act, int I, int64_t total)
+qk_norm_rope_kernel(const float* __restrict__ qkv, int S, const uint16_t* __restrict__ wq,
+                    const uint16_t* __restrict__ wk, const int32_t* __restrict__ lens, int K,
+                    uint16_t* __restrict__ q, uint16_t* __restrict__ k, uint16_t* __restrict__ v,
+                    int R, int Hq, int Hkv, float eps, double log_theta)
 {
+    constexpr int D = 128;
+    const int heads = Hq + 2 * Hkv;
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= R * heads) return;
+    const int lane = threadIdx.x & 63;
+    const int r = item / heads;
+    const int h = item % heads;
+    const int64_t i = (int64_t)r * heads * D + (int64_t)h * D + lane;
+    float x0 = qkv[i], x1 = qkv[i + 64];
+    const int64_t stride = (int64_t)R * heads * D;
+#pragma unroll 8
+    for (int s = 1; s < S; ++s) {
+        x0 += qkv[s * stride + i];
+        x1 += qkv[s * stride + i + 64];
+    }
+    qk_norm_rope_item(x0, x1, r, h, lane, wq, wk, lens, K, q, k, v, Hq, Hkv, eps, log_theta);
+}
+
+// ---------------------------------------------------------------- SwiGLU
+// act[r][i] = silu(g) * u, g = gu[r][i], u = gu[r][I + i], silu(g) =
+// g / (1 + e^-g); gu holds S >= 1 partial sums [S][R][2I] of the gate/up
+// projection (S = 1: the projection itself), added in split order first.
+// One thread per four consecutive i (I a multiple of 4).
+__global__ void __launch_bounds__(256)
+swiglu_kernel(const float* __restrict__ gu, int S, uint16_t* __restrict__ act, int R, int I)
+{
+    const int I4 = I / 4;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= total) return;
-    const int64_t r = t / I;
-    const int i = (int)(t % I);
-    const float g = gu[r * 2 * I + i];
-    const float u = gu[r * 2 * I + I + i];
-    const float a = g / (1.f + expf(-g)) * u;
-    act[t] = (uint16_t)(pack_bf16x2(a, 0.f) & 0xffffu);
+    if (t >= (int64_t)R * I4) return;
+    const int64_t r = t / I4;
+    const int i = (int)(t % I4) * 4;
+    const int64_t stride = (int64_t)R * 2 * I;
+    const f32x4 g = sum_splits(gu, S, stride, r * 2 * I + i);
+    const f32x4 u = sum_splits(gu, S, stride, r * 2 * I + I + i);
+    float a[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a[c] = g[c] / (1.f + expf(-g[c])) * u[c];
+    *(u32x2*)(act + r * I + i) = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
 }
 
 // ----------------------------------------------------- block input tokens
@@ -292,6 +399,82 @@ using namespace orthrus;
 
 extern "C" {
 
+namespace {
+
+bool mis16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+bool mis8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) != 0; }
+
+// Shape checks shared by the projections.
+int gemm_check(const void* x, const void* w, int R, int N, int Kin)
+{
+    if (!x || !w) return ORTHRUS_ERR_NULL;
+    if (R < 1 || N < 1 || Kin < 1) return ORTHRUS_ERR_SHAPE;
+    if (Kin % kGemmHC || N % 4 || R > 65535 * 128) return ORTHRUS_ERR_UNSUPPORTED;
+    if (mis16(x) || mis16(w)) return ORTHRUS_ERR_UNSUPPORTED;
+    return ORTHRUS_OK;
+}
+
+// The projection's main launch: out_mode 0 writes the S partial sums to
+// part, 1 / 2 write y (fp32 / bf16, + res) directly (S = 1 only).
+int gemm_main(const void* x, const void* w, int R, int N, int Kin, int S, int mode, float* part,
+              void* y, const float* res, hipStream_t stream)
+{
+    const int cps = Kin / kGemmHC / S;
+    const uint16_t *xp = static_cast<const uint16_t*>(x), *wp = static_cast<const uint16_t*>(w);
+    const unsigned gx = (unsigned)((N + kGemmNB - 1) / kGemmNB);
+    if (R <= 32)
+        hipLaunchKernelGGL((gemm_kernel<3, 32>), dim3(gx, 1, S), dim3(256), 0, stream, xp, wp, R,
+                           N, Kin, cps, mode, part, y, res);
+    else if (R <= 64)
+        hipLaunchKernelGGL((gemm_kernel<3, 64>), dim3(gx, 1, S), dim3(256), 0, stream, xp, wp, R,
+                           N, Kin, cps, mode, part, y, res);
+    else
+        hipLaunchKernelGGL((gemm_kernel<2, 128>), dim3(gx, (unsigned)((R + 127) / 128), S),
+                           dim3(256), 0, stream, xp, wp, R, N, Kin, cps, mode, part, y, res);
+    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+// The partial sums of a fused projection: always written, even with S = 1.
+size_t partial_bytes(int R, int N, int Kin)
+{
+    return (size_t)gemm_splits(N, Kin) * (size_t)R * (size_t)N * sizeof(float);
+}
+
+int partial_check(void* ws, size_t ws_bytes, int R, int N, int Kin)
+{
+    if (!ws || ws_bytes < partial_bytes(R, N, Kin) || mis16(ws)) return ORTHRUS_ERR_WORKSPACE;
+    return ORTHRUS_OK;
+}
+
+int norm_groups(int H) { return (H / 4 + kNormThreads - 1) / kNormThreads; }
+
+int launch_norm(const float* part, int S, int64_t RN, const float* res, float* h,
+                const uint16_t* w, uint16_t* y, int R, int H, float eps, hipStream_t stream)
+{
+    const int ng = norm_groups(H);
+    const dim3 grid((unsigned)R), block(kNormThreads);
+#define ORTHRUS_NORM(NG)                                                                        \
+    if (part)                                                                                   \
+        hipLaunchKernelGGL((reduce_rmsnorm_kernel<NG>), grid, block, 0, stream, part, S, RN,   \
+                           res, h, w, y, H, eps);                                               \
+    else                                                                                        \
+        hipLaunchKernelGGL((rmsnorm_kernel<NG>), grid, block, 0, stream, h, w, y, H, eps);
+    if (ng <= 1) { ORTHRUS_NORM(1) }
+    else if (ng <= 2) { ORTHRUS_NORM(2) }
+    else { ORTHRUS_NORM(4) }
+#undef ORTHRUS_NORM
+    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+int norm_check(int H, float eps)
+{
+    if (H < 4 || !(eps > 0.f)) return ORTHRUS_ERR_SHAPE;
+    if (H % 4 || H / 4 > kNormMaxGroups * kNormThreads) return ORTHRUS_ERR_UNSUPPORTED;
+    return ORTHRUS_OK;
+}
+
+}  // namespace
+
 size_t orthrus_gemm_workspace_bytes(int R, int N, int Kin)
 {
     if (R < 1 || N < 1 || Kin < kGemmHC || Kin % kGemmHC || N % 4) return 0;
@@ -299,81 +482,155 @@ size_t orthrus_gemm_workspace_bytes(int R, int N, int Kin)
     return S > 1 ? (size_t)S * R * N * sizeof(float) : 0;
 }
 
+size_t orthrus_gemm_epilogue_workspace_bytes(int R, int N, int Kin)
+{
+    if (R < 1 || N < 1 || Kin < kGemmHC || Kin % kGemmHC || N % 4) return 0;
+    return partial_bytes(R, N, Kin);
+}
+
 int orthrus_gemm(const void *x, const void *w, const float *residual, void *y, int R, int N,
                  int Kin, int out_dtype, void *workspace, size_t workspace_bytes,
                  hipStream_t stream)
 {
-    if (!x || !w || !y) return ORTHRUS_ERR_NULL;
+    if (!y) return ORTHRUS_ERR_NULL;
+    int st = gemm_check(x, w, R, N, Kin);
+    if (st != ORTHRUS_OK) return st;
     if (out_dtype != ORTHRUS_F32 && out_dtype != ORTHRUS_BF16) return ORTHRUS_ERR_DTYPE;
-    if (R < 1 || N < 1 || Kin < 1) return ORTHRUS_ERR_SHAPE;
-    if (Kin % kGemmHC || N % 4 || R > 65535 * 128 || N > (1 << 28) / 1) return ORTHRUS_ERR_UNSUPPORTED;
-    if ((reinterpret_cast<uintptr_t>(x) & 15u) || (reinterpret_cast<uintptr_t>(w) & 15u) ||
-        (reinterpret_cast<uintptr_t>(y) & 15u) || (reinterpret_cast<uintptr_t>(residual) & 15u))
-        return ORTHRUS_ERR_UNSUPPORTED;
+    if (mis16(y) || mis16(residual)) return ORTHRUS_ERR_UNSUPPORTED;
     const int S = gemm_splits(N, Kin);
     const size_t need = S > 1 ? (size_t)S * R * N * sizeof(float) : 0;
-    if (need && (!workspace || workspace_bytes < need ||
-                 (reinterpret_cast<uintptr_t>(workspace) & 15u)))
+    if (need && (!workspace || workspace_bytes < need || mis16(workspace)))
         return ORTHRUS_ERR_WORKSPACE;
-    const int cps = Kin / kGemmHC / S;
     const int mode = S > 1 ? 0 : (out_dtype == ORTHRUS_F32 ? 1 : 2);
-    const uint16_t *xp = static_cast<const uint16_t *>(x), *wp = static_cast<const uint16_t *>(w);
     float *part = static_cast<float *>(workspace);
-    const unsigned gx = (unsigned)((N + kGemmNB - 1) / kGemmNB);
-    if (R <= 32)
-        hipLaunchKernelGGL((gemm_kernel<3, 32>), dim3(gx, 1, S), dim3(256), 0, stream, xp, wp, R,
-                           N, Kin, cps, mode, part, y, residual);
-    else if (R <= 64)
-        hipLaunchKernelGGL((gemm_kernel<3, 64>), dim3(gx, 1, S), dim3(256), 0, stream, xp, wp, R,
-                           N, Kin, cps, mode, part, y, residual);
-    else
-        hipLaunchKernelGGL((gemm_kernel<2, 128>), dim3(gx, (unsigned)((R + 127) / 128), S),
-                           dim3(256), 0, stream, xp, wp, R, N, Kin, cps, mode, part, y, residual);
-    if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
-    if (S > 1) {
-        const int64_t rn4 = (int64_t)R * N / 4;
-        hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((rn4 + 255) / 256)), dim3(256), 0,
-                           stream, part, S, rn4, out_dtype == ORTHRUS_BF16 ? 1 : 0, y, residual);
-        if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
-    }
-    return ORTHRUS_OK;
+    st = gemm_main(x, w, R, N, Kin, S, mode, part, y, residual, stream);
+    if (st != ORTHRUS_OK || S == 1) return st;
+    const int64_t rn4 = (int64_t)R * N / 4;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((rn4 + 255) / 256)), dim3(256), 0,
+                       stream, part, S, rn4, out_dtype == ORTHRUS_BF16 ? 1 : 0, y, residual);
+    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }
 
 int orthrus_rmsnorm(const float *x, const void *weight, void *y, int R, int H, float eps,
                     hipStream_t stream)
 {
     if (!x || !weight || !y) return ORTHRUS_ERR_NULL;
-    if (R < 1 || H < 1 || !(eps > 0.f)) return ORTHRUS_ERR_SHAPE;
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)R), dim3(256), 0, stream, x,
-                       static_cast<const uint16_t *>(weight), static_cast<uint16_t *>(y), H, eps);
-    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+    if (R < 1) return ORTHRUS_ERR_SHAPE;
+    const int st = norm_check(H, eps);
+    if (st != ORTHRUS_OK) return st;
+    if (mis16(x) || mis8(weight) || mis8(y)) return ORTHRUS_ERR_UNSUPPORTED;
+    return launch_norm(nullptr, 0, 0, nullptr, const_cast<float *>(x),
+                       static_cast<const uint16_t *>(weight), static_cast<uint16_t *>(y), R, H,
+                       eps, stream);
 }
 
-int orthrus_qk_norm_rope(const float *qkv, const void *q_norm, const void *k_norm,
-                         const int32_t *lens, int K, void *q, void *k, void *v, int R, int Hq,
-                         int Hkv, int D, float eps, float rope_theta, hipStream_t stream)
+int orthrus_gemm_rmsnorm(const void *x, const void *w, float *h, const void *norm_weight,
+                         void *xn, int R, int H, int Kin, float eps, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream)
 {
-    if (!qkv || !q_norm || !k_norm || !lens || !q || !k || !v) return ORTHRUS_ERR_NULL;
+    if (!h || !norm_weight || !xn) return ORTHRUS_ERR_NULL;
+    int st = gemm_check(x, w, R, H, Kin);
+    if (st != ORTHRUS_OK) return st;
+    if ((st = norm_check(H, eps)) != ORTHRUS_OK) return st;
+    if (mis16(h) || mis8(norm_weight) || mis8(xn)) return ORTHRUS_ERR_UNSUPPORTED;
+    if ((st = partial_check(workspace, workspace_bytes, R, H, Kin)) != ORTHRUS_OK) return st;
+    const int S = gemm_splits(H, Kin);
+    float *part = static_cast<float *>(workspace);
+    if ((st = gemm_main(x, w, R, H, Kin, S, 0, part, nullptr, nullptr, stream)) != ORTHRUS_OK)
+        return st;
+    return launch_norm(part, S, (int64_t)R * H, h, h, static_cast<const uint16_t *>(norm_weight),
+                       static_cast<uint16_t *>(xn), R, H, eps, stream);
+}
+
+namespace {
+
+int qk_check(const void *q_norm, const void *k_norm, const int32_t *lens, int K, const void *q,
+             const void *k, const void *v, int R, int Hq, int Hkv, int D, float eps,
+             float rope_theta)
+{
+    if (!q_norm || !k_norm || !lens || !q || !k || !v) return ORTHRUS_ERR_NULL;
     if (R < 1 || K < 1 || R % K || Hq < 1 || Hkv < 1 || !(eps > 0.f) || !(rope_theta > 1.f))
         return ORTHRUS_ERR_SHAPE;
     if (D != 128) return ORTHRUS_ERR_UNSUPPORTED;
+    return ORTHRUS_OK;
+}
+
+int launch_qk(const float *qkv, int S, const void *q_norm, const void *k_norm,
+              const int32_t *lens, int K, void *q, void *k, void *v, int R, int Hq, int Hkv,
+              float eps, float rope_theta, hipStream_t stream)
+{
     const int64_t items = (int64_t)R * (Hq + 2 * Hkv);
     hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, stream,
-                       qkv, static_cast<const uint16_t *>(q_norm),
+                       qkv, S, static_cast<const uint16_t *>(q_norm),
                        static_cast<const uint16_t *>(k_norm), lens, K,
                        static_cast<uint16_t *>(q), static_cast<uint16_t *>(k),
                        static_cast<uint16_t *>(v), R, Hq, Hkv, eps, std::log((double)rope_theta));
     return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }
 
+int launch_swiglu(const float *gu, int S, void *act, int R, int I, hipStream_t stream)
+{
+    const int64_t total = (int64_t)R * (I / 4);
+    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       gu, S, static_cast<uint16_t *>(act), R, I);
+    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+}  // namespace
+
+int orthrus_qk_norm_rope(const float *qkv, const void *q_norm, const void *k_norm,
+                         const int32_t *lens, int K, void *q, void *k, void *v, int R, int Hq,
+                         int Hkv, int D, float eps, float rope_theta, hipStream_t stream)
+{
+    if (!qkv) return ORTHRUS_ERR_NULL;
+    const int st = qk_check(q_norm, k_norm, lens, K, q, k, v, R, Hq, Hkv, D, eps, rope_theta);
+    if (st != ORTHRUS_OK) return st;
+    return launch_qk(qkv, 1, q_norm, k_norm, lens, K, q, k, v, R, Hq, Hkv, eps, rope_theta,
+                     stream);
+}
+
+int orthrus_gemm_qk_norm_rope(const void *x, const void *w_qkv, const void *q_norm,
+                              const void *k_norm, const int32_t *lens, int K, void *q, void *k,
+                              void *v, int R, int Hq, int Hkv, int D, int Kin, float eps,
+                              float rope_theta, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream)
+{
+    int st = qk_check(q_norm, k_norm, lens, K, q, k, v, R, Hq, Hkv, D, eps, rope_theta);
+    if (st != ORTHRUS_OK) return st;
+    const int N = (Hq + 2 * Hkv) * D;
+    if ((st = gemm_check(x, w_qkv, R, N, Kin)) != ORTHRUS_OK) return st;
+    if ((st = partial_check(workspace, workspace_bytes, R, N, Kin)) != ORTHRUS_OK) return st;
+    const int S = gemm_splits(N, Kin);
+    float *part = static_cast<float *>(workspace);
+    if ((st = gemm_main(x, w_qkv, R, N, Kin, S, 0, part, nullptr, nullptr, stream)) != ORTHRUS_OK)
+        return st;
+    return launch_qk(part, S, q_norm, k_norm, lens, K, q, k, v, R, Hq, Hkv, eps, rope_theta,
+                     stream);
+}
+
 int orthrus_swiglu(const float *gate_up, void *act, int R, int I, hipStream_t stream)
 {
     if (!gate_up || !act) return ORTHRUS_ERR_NULL;
     if (R < 1 || I < 1) return ORTHRUS_ERR_SHAPE;
-    const int64_t total = (int64_t)R * I;
-    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       gate_up, static_cast<uint16_t *>(act), I, total);
-    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+    if (I % 4 || mis16(gate_up) || mis8(act)) return ORTHRUS_ERR_UNSUPPORTED;
+    return launch_swiglu(gate_up, 1, act, R, I, stream);
+}
+
+int orthrus_gemm_swiglu(const void *x, const void *w_gate_up, void *act, int R, int I, int Kin,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!act) return ORTHRUS_ERR_NULL;
+    if (I < 1) return ORTHRUS_ERR_SHAPE;
+    int st = gemm_check(x, w_gate_up, R, 2 * I, Kin);
+    if (st != ORTHRUS_OK) return st;
+    if (I % 4 || mis8(act)) return ORTHRUS_ERR_UNSUPPORTED;
+    if ((st = partial_check(workspace, workspace_bytes, R, 2 * I, Kin)) != ORTHRUS_OK) return st;
+    const int S = gemm_splits(2 * I, Kin);
+    float *part = static_cast<float *>(workspace);
+    if ((st = gemm_main(x, w_gate_up, R, 2 * I, Kin, S, 0, part, nullptr, nullptr, stream)) !=
+        ORTHRUS_OK)
+        return st;
+    return launch_swiglu(part, S, act, R, I, stream);
 }
 
 int orthrus_block_tokens(const int32_t *anchor, const int32_t *cand, int32_t fill,

@@ -80,11 +80,9 @@ class DecodeModel:
         self.vb_scratch = torch.empty_like(self.kb_scratch)
         self.h = torch.empty((R, d.H), **f32)
         self.x = torch.empty((R, d.H), **bf)
-        self.qkv = torch.empty((R, nqkv), **f32)
         self.q = torch.empty((B, K, d.Hq, d.D), **bf)
         self.o = torch.empty((B, K, d.Hq, d.D), **bf)
         self.lse = torch.empty((B, d.Hq, K), **f32)
-        self.gu = torch.empty((R, 2 * d.I), **f32)
         self.act = torch.empty((R, d.I), **bf)
         self.tok = torch.empty((B, K), **i32)          # a decode block
         self.d_tok = torch.empty((B, K), **i32)
@@ -94,7 +92,8 @@ class DecodeModel:
         self.n_emit = torch.empty(B, **i32)
         self.emit_off = torch.empty(B + 1, **i32)
         self.emitted = torch.empty(B * K, **i32)
-        gws = max(B_.orthrus_gemm_workspace_bytes(R, n, k) for n, k in
+        # the projections' partial sums (each projection's epilogue reads them)
+        gws = max(B_.orthrus_gemm_epilogue_workspace_bytes(R, n, k) for n, k in
                   ((nqkv, d.H), (d.H, d.Hq * d.D), (2 * d.I, d.H), (d.H, d.I)))
         self.gws = torch.empty(max(gws, 16), dtype=torch.uint8, device=dev)
         self.aws, _ = api.block_attn_workspace(self.caches[0], B, K, d.Hq, d.Hkv, d.D, B_.BF16,
@@ -104,35 +103,34 @@ class DecodeModel:
         self.views_attn = {}
 
     # ------------------------------------------------------------ kernels
-    def _gemm(self, x, w, y, res, N, Kin, out_dtype):
-        R = x.shape[0]
-        _ok("orthrus_gemm", B_.orthrus_gemm(x, w, res, y, R, N, Kin, out_dtype, self.gws,
-                                            self.gws.numel()))
-
-    def _layer(self, l, view, mask, kb, vb, K):
+    def _layer(self, l, view, mask, kb, vb, K, next_norm):
+        """Layer l on the block rows, whose normed input x = rmsnorm(h) the
+        previous projection's epilogue wrote; ends with x = next_norm(h)."""
         d, w = self.d, self.w
         R = self.B * K
-        nqkv = (d.Hq + 2 * d.Hkv) * d.D
         h, x = self.h[:R], self.x[:R]
-        _ok("orthrus_rmsnorm", B_.orthrus_rmsnorm(h, w[f"l{l}.in_norm"], x, R, d.H, d.eps))
-        self._gemm(x, w[f"l{l}.{view}.wqkv"], self.qkv[:R], None, nqkv, d.H, B_.F32)
+        ws, wn = self.gws, self.gws.numel()
         q = self.q[:, :K] if K == self.K else torch.empty((self.B, K, d.Hq, d.D),
                                                           dtype=torch.bfloat16,
                                                           device=self.h.device)
-        _ok("orthrus_qk_norm_rope",
-            B_.orthrus_qk_norm_rope(self.qkv[:R], w[f"l{l}.q_norm"], w[f"l{l}.k_norm"], self.lens,
-                                    K, q, kb, vb, R, d.Hq, d.Hkv, d.D, d.eps, d.theta))
+        _ok("orthrus_gemm_qk_norm_rope",
+            B_.orthrus_gemm_qk_norm_rope(x, w[f"l{l}.{view}.wqkv"], w[f"l{l}.q_norm"],
+                                         w[f"l{l}.k_norm"], self.lens, K, q, kb, vb, R, d.Hq,
+                                         d.Hkv, d.D, d.H, d.eps, d.theta, ws, wn))
         o = self.o if K == self.K else torch.empty_like(q)
         lse = self.lse if K == self.K else torch.empty((self.B, d.Hq, K), dtype=torch.float32,
                                                        device=self.h.device)
         api.block_attn(q, kb, vb, self.caches[l], mask=mask, scale=d.D ** -0.5, out=o, lse=lse,
                        workspace=self.aws if K == self.K else None)
-        # h += o Wo^T (in place), then the MLP
-        self._gemm(o.view(R, d.Hq * d.D), w[f"l{l}.{view}.wo"], h, h, d.H, d.Hq * d.D, B_.F32)
-        _ok("orthrus_rmsnorm", B_.orthrus_rmsnorm(h, w[f"l{l}.post_norm"], x, R, d.H, d.eps))
-        self._gemm(x, w[f"l{l}.wgu"], self.gu[:R], None, 2 * d.I, d.H, B_.F32)
-        _ok("orthrus_swiglu", B_.orthrus_swiglu(self.gu[:R], self.act[:R], R, d.I))
-        self._gemm(self.act[:R], w[f"l{l}.wdown"], h, h, d.H, d.I, B_.F32)
+        # h += o Wo^T (in place), x = post_norm(h); then the MLP
+        _ok("orthrus_gemm_rmsnorm",
+            B_.orthrus_gemm_rmsnorm(o.view(R, d.Hq * d.D), w[f"l{l}.{view}.wo"], h,
+                                    w[f"l{l}.post_norm"], x, R, d.H, d.Hq * d.D, d.eps, ws, wn))
+        _ok("orthrus_gemm_swiglu",
+            B_.orthrus_gemm_swiglu(x, w[f"l{l}.wgu"], self.act[:R], R, d.I, d.H, ws, wn))
+        _ok("orthrus_gemm_rmsnorm",
+            B_.orthrus_gemm_rmsnorm(self.act[:R], w[f"l{l}.wdown"], h, next_norm, x, R, d.H, d.I,
+                                    d.eps, ws, wn))
 
     def forward(self, tokens, view, mask, kv_out=None, idx=None):
         """One view's pass over the block tokens [B, K'] (device int32) at
@@ -147,6 +145,8 @@ class DecodeModel:
             raise ValueError(f"a block of {B} x {K} rows does not fit the {self.R_max}-row "
                              f"buffers of this {self.B}-request model")
         _ok("orthrus_embed", B_.orthrus_embed(tokens, w["embed"], self.h[:R], R, d.H))
+        x = self.x[:R]
+        _ok("orthrus_rmsnorm", B_.orthrus_rmsnorm(self.h[:R], w["l0.in_norm"], x, R, d.H, d.eps))
         for l in range(d.layers):
             if kv_out is not None:
                 kb, vb = kv_out[l]
@@ -155,9 +155,8 @@ class DecodeModel:
             else:
                 kb = torch.empty((B, K, d.Hkv, d.D), dtype=torch.bfloat16, device=self.h.device)
                 vb = torch.empty_like(kb)
-            self._layer(l, view, mask, kb, vb, K)
-        x = self.x[:R]
-        _ok("orthrus_rmsnorm", B_.orthrus_rmsnorm(self.h[:R], w["final_norm"], x, R, d.H, d.eps))
+            nxt = w[f"l{l + 1}.in_norm"] if l + 1 < d.layers else w["final_norm"]
+            self._layer(l, view, mask, kb, vb, K, nxt)
         if idx is not None:
             api.lmhead_argmax(x, w["lm_head"], idx=idx.view(-1),
                               workspace=self.lws if K == self.K else None)

@@ -376,9 +376,54 @@ int orthrus_gemm(const void *x, const void *w, const float *residual, void *y,
 size_t orthrus_gemm_workspace_bytes(int R, int N, int Kin);
 
 /* orthrus_rmsnorm -- y[r] = x[r] / sqrt(mean_k x[r][k]^2 + eps) * weight:
- * x fp32 [R][H], weight bf16 [H], y bf16 [R][H]. */
+ * x fp32 [R][H], weight bf16 [H], y bf16 [R][H].  The sum of squares of a
+ * row is formed in one fixed order that depends on H only.  H a multiple of
+ * 4 and at most 16384; x 16-byte, weight and y 8-byte aligned. */
 int orthrus_rmsnorm(const float *x, const void *weight, void *y, int R, int H,
                     float eps, hipStream_t stream);
+
+/*
+ * The projections with the operation that follows each of them in the layer,
+ * fused into the second pass that adds the partial sums of the split input
+ * dimension.  Each gives, bit for bit, what orthrus_gemm (fp32 output)
+ * followed by the separate kernel gives: the partial sums are added in split
+ * order and the epilogue's arithmetic is the separate kernel's.  They always
+ * write the partial sums (also when the input dimension is not split), so
+ * workspace >= orthrus_gemm_epilogue_workspace_bytes(R, N, Kin) bytes,
+ * 16-byte aligned, with N the projection's output width.  Same x / W
+ * contract as orthrus_gemm (Kin a multiple of 64, 16-byte aligned).
+ */
+size_t orthrus_gemm_epilogue_workspace_bytes(int R, int N, int Kin);
+
+/* orthrus_gemm_rmsnorm -- the output (or down) projection with the residual
+ * and the next RMSNorm: h += x W^T in place (fp32 [R][H], W bf16 [H][Kin]),
+ * then xn = rmsnorm(h) * norm_weight (bf16 [R][H]).  = orthrus_gemm(x, W, h,
+ * h, R, H, Kin, F32) then orthrus_rmsnorm(h, norm_weight, xn, R, H, eps).
+ * H as for orthrus_rmsnorm; h 16-byte, norm_weight and xn 8-byte aligned. */
+int orthrus_gemm_rmsnorm(const void *x, const void *w, float *h,
+                         const void *norm_weight, void *xn, int R, int H,
+                         int Kin, float eps, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* orthrus_gemm_swiglu -- the MLP's gate/up projection and SwiGLU: W bf16
+ * [2I][Kin] (the I gate rows, then the I up rows), act bf16 [R][I] =
+ * orthrus_gemm(x, W, NULL, gu, R, 2I, Kin, F32) then orthrus_swiglu(gu, act,
+ * R, I), without the fp32 gu ever being written.  I a multiple of 4; act
+ * 8-byte aligned. */
+int orthrus_gemm_swiglu(const void *x, const void *w_gate_up, void *act, int R,
+                        int I, int Kin, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* orthrus_gemm_qk_norm_rope -- the QKV projection (W bf16 [(Hq+2Hkv)*D][Kin])
+ * and orthrus_qk_norm_rope on its output, without the fp32 projection ever
+ * being written: = orthrus_gemm(x, W, NULL, qkv, R, (Hq+2Hkv)*D, Kin, F32)
+ * then orthrus_qk_norm_rope(qkv, ...).  Arguments as for those two. */
+int orthrus_gemm_qk_norm_rope(const void *x, const void *w_qkv,
+                              const void *q_norm, const void *k_norm,
+                              const int32_t *lens, int K, void *q, void *k,
+                              void *v, int R, int Hq, int Hkv, int D, int Kin,
+                              float eps, float rope_theta, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* orthrus_qk_norm_rope -- from the fp32 projection qkv [R][(Hq+2Hkv)*D]
  * (q heads, then k heads, then v heads) of a block's rows (row r is block
@@ -402,7 +447,8 @@ int orthrus_block_tokens(const int32_t *anchor, const int32_t *cand,
                          hipStream_t stream);
 
 /* orthrus_swiglu -- act[r][i] = silu(gate_up[r][i]) * gate_up[r][I + i],
- * silu(g) = g / (1 + e^-g): gate_up fp32 [R][2I], act bf16 [R][I]. */
+ * silu(g) = g / (1 + e^-g): gate_up fp32 [R][2I], act bf16 [R][I].  I a
+ * multiple of 4; gate_up 16-byte, act 8-byte aligned. */
 int orthrus_swiglu(const float *gate_up, void *act, int R, int I,
                    hipStream_t stream);
 

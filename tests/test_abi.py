@@ -237,6 +237,55 @@ def test_stream_read_validation():
     assert f(FAKE, 1024, 70000, FAKE, None) == B.ERR_UNSUPPORTED
 
 
+def test_layer_validation_codes():
+    L = B.lib()
+    # orthrus_rmsnorm: H a multiple of 4, at most 16384; eps > 0
+    assert L.orthrus_rmsnorm(None, FAKE, FAKE, 4, 4096, 1e-6, None) == B.ERR_NULL
+    assert L.orthrus_rmsnorm(FAKE, FAKE, FAKE, 0, 4096, 1e-6, None) == B.ERR_SHAPE
+    assert L.orthrus_rmsnorm(FAKE, FAKE, FAKE, 4, 4096, 0.0, None) == B.ERR_SHAPE
+    assert L.orthrus_rmsnorm(FAKE, FAKE, FAKE, 4, 4094, 1e-6, None) == B.ERR_UNSUPPORTED
+    assert L.orthrus_rmsnorm(FAKE, FAKE, FAKE, 4, 16388, 1e-6, None) == B.ERR_UNSUPPORTED
+    assert L.orthrus_rmsnorm(FAKE + 8, FAKE, FAKE, 4, 4096, 1e-6, None) == B.ERR_UNSUPPORTED
+    assert L.orthrus_swiglu(FAKE, FAKE, 4, 1002, None) == B.ERR_UNSUPPORTED
+    # the fused projections: partial sums always written
+    ew = B.orthrus_gemm_epilogue_workspace_bytes
+    assert ew(32, 4096, 4096) == 16 * 32 * 4096 * 4           # split 16 ways
+    assert ew(32, 24576, 4096) == 2 * 32 * 24576 * 4           # split 2 ways
+    assert ew(7, 264, 64) == 7 * 264 * 4                        # not split, still written
+    assert ew(32, 4096, 100) == 0
+    assert B.orthrus_gemm_workspace_bytes(7, 264, 64) == 0
+    g = L.orthrus_gemm_rmsnorm
+    need = ew(32, 4096, 4096)
+    assert g(None, FAKE, FAKE, FAKE, FAKE, 32, 4096, 4096, 1e-6, FAKE, need, None) == B.ERR_NULL
+    assert g(FAKE, FAKE, None, FAKE, FAKE, 32, 4096, 4096, 1e-6, FAKE, need, None) == B.ERR_NULL
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 32, 4096, 4000, 1e-6, FAKE, need,
+             None) == B.ERR_UNSUPPORTED                          # Kin not a multiple of 64
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 32, 4098, 4096, 1e-6, FAKE, need,
+             None) == B.ERR_UNSUPPORTED                          # H not a multiple of 4
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 32, 4096, 4096, 1e-6, FAKE, need - 4,
+             None) == B.ERR_WORKSPACE
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 32, 4096, 4096, 1e-6, None, need,
+             None) == B.ERR_WORKSPACE
+    sw = L.orthrus_gemm_swiglu
+    need = ew(32, 24576, 4096)
+    assert sw(FAKE, FAKE, None, 32, 12288, 4096, FAKE, need, None) == B.ERR_NULL
+    assert sw(FAKE, FAKE, FAKE, 32, 0, 4096, FAKE, need, None) == B.ERR_SHAPE
+    assert sw(FAKE, FAKE, FAKE, 32, 12286, 4096, FAKE, need, None) == B.ERR_UNSUPPORTED
+    assert sw(FAKE, FAKE, FAKE, 32, 12288, 4096, FAKE, need - 1, None) == B.ERR_WORKSPACE
+    qk = L.orthrus_gemm_qk_norm_rope
+    need = ew(32, 6144, 4096)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 32, FAKE, FAKE, FAKE, 32, 32, 8, 128, 4096, 1e-6, 1e6,
+            FAKE, need, None]
+    bad = list(args); bad[4] = None
+    assert qk(*bad) == B.ERR_NULL                                # lens
+    bad = list(args); bad[9] = 33
+    assert qk(*bad) == B.ERR_SHAPE                               # R not a multiple of K
+    bad = list(args); bad[12] = 64
+    assert qk(*bad) == B.ERR_UNSUPPORTED                         # D = 128 only
+    bad = list(args); bad[17] = need - 4
+    assert qk(*bad) == B.ERR_WORKSPACE
+
+
 def test_single_hip_runtime_in_process():
     import torch  # noqa: F401
     B.lib()

@@ -129,6 +129,88 @@ def test_qk_norm_rope(B, K, lens):
         assert (err <= bound).all(), (name, float((err / bound).max()))
 
 
+def _ws(n):
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("R,H,Kin", [
+    (32, 4096, 4096),      # output projection: split 16 ways
+    (32, 4096, 12288),     # down projection: split 16 ways
+    (5, 256, 64),          # not split; one float4 group per thread, most threads idle
+    (3, 8192, 128),        # two groups per thread
+    (2, 16384, 64),        # four groups per thread (the largest H)
+])
+def test_gemm_rmsnorm_equals_gemm_then_rmsnorm(R, H, Kin):
+    gen = torch.Generator().manual_seed(R * 13 + H + Kin)
+    x, w = bf((R, Kin), gen).to(DEV), bf((H, Kin), gen, Kin ** -0.5).to(DEV)
+    nw = bf((H,), gen).to(DEV)
+    h0 = (torch.randn((R, H), generator=gen) * 2).to(DEV)
+    say(f"gemm_rmsnorm R={R} H={H} Kin={Kin}")
+    ha, xa = h0.clone(), torch.empty((R, H), dtype=torch.bfloat16, device=DEV)
+    ws = _ws(B_.orthrus_gemm_workspace_bytes(R, H, Kin))
+    B_.check("gemm", B_.orthrus_gemm(x, w, ha, ha, R, H, Kin, B_.F32, ws, ws.numel()))
+    B_.check("rmsnorm", B_.orthrus_rmsnorm(ha, nw, xa, R, H, 1e-6))
+    hb, xb = h0.clone(), torch.empty((R, H), dtype=torch.bfloat16, device=DEV)
+    ws2 = _ws(B_.orthrus_gemm_epilogue_workspace_bytes(R, H, Kin))
+    B_.check("gemm_rmsnorm", B_.orthrus_gemm_rmsnorm(x, w, hb, nw, xb, R, H, Kin, 1e-6, ws2,
+                                                     ws2.numel()))
+    torch.cuda.synchronize()
+    assert torch.equal(ha, hb)
+    assert torch.equal(xa, xb)
+    # and the norm itself against fp64
+    ref = M.rmsnorm(hb.double().cpu().numpy(), nw.double().cpu().numpy(), 1e-6)
+    err = np.abs(xb.double().cpu().numpy() - ref)
+    assert (err <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max()).all()
+
+
+@pytest.mark.parametrize("R,I,Kin", [(32, 12288, 4096), (7, 132, 64), (40, 1024, 512)])
+def test_gemm_swiglu_equals_gemm_then_swiglu(R, I, Kin):
+    gen = torch.Generator().manual_seed(R + I + Kin)
+    x, w = bf((R, Kin), gen).to(DEV), bf((2 * I, Kin), gen, Kin ** -0.5).to(DEV)
+    say(f"gemm_swiglu R={R} I={I} Kin={Kin}")
+    gu = torch.empty((R, 2 * I), dtype=torch.float32, device=DEV)
+    ws = _ws(B_.orthrus_gemm_workspace_bytes(R, 2 * I, Kin))
+    B_.check("gemm", B_.orthrus_gemm(x, w, None, gu, R, 2 * I, Kin, B_.F32, ws, ws.numel()))
+    a1 = torch.empty((R, I), dtype=torch.bfloat16, device=DEV)
+    B_.check("swiglu", B_.orthrus_swiglu(gu, a1, R, I))
+    a2 = torch.empty_like(a1)
+    ws2 = _ws(B_.orthrus_gemm_epilogue_workspace_bytes(R, 2 * I, Kin))
+    B_.check("gemm_swiglu", B_.orthrus_gemm_swiglu(x, w, a2, R, I, Kin, ws2, ws2.numel()))
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2)
+
+
+@pytest.mark.parametrize("B,K,Kin,lens", [(1, 32, 4096, [8192]), (3, 5, 256, [0, 17, 100000])])
+def test_gemm_qk_norm_rope_equals_gemm_then_qk_norm_rope(B, K, Kin, lens):
+    gen = torch.Generator().manual_seed(B * 100 + K)
+    Hq, Hkv, D = 32, 8, 128
+    R, N = B * K, (Hq + 2 * Hkv) * D
+    x, w = bf((R, Kin), gen).to(DEV), bf((N, Kin), gen, Kin ** -0.5).to(DEV)
+    wq, wk = bf((D,), gen).to(DEV), bf((D,), gen).to(DEV)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    say(f"gemm_qk_norm_rope B={B} K={K} Kin={Kin}")
+    qkv = torch.empty((R, N), dtype=torch.float32, device=DEV)
+    ws = _ws(B_.orthrus_gemm_workspace_bytes(R, N, Kin))
+    B_.check("gemm", B_.orthrus_gemm(x, w, None, qkv, R, N, Kin, B_.F32, ws, ws.numel()))
+    outs = []
+    for fused in (False, True):
+        q = torch.empty((R, Hq, D), dtype=torch.bfloat16, device=DEV)
+        k = torch.empty((R, Hkv, D), dtype=torch.bfloat16, device=DEV)
+        v = torch.empty((R, Hkv, D), dtype=torch.bfloat16, device=DEV)
+        if fused:
+            ws2 = _ws(B_.orthrus_gemm_epilogue_workspace_bytes(R, N, Kin))
+            B_.check("gemm_qk", B_.orthrus_gemm_qk_norm_rope(x, w, wq, wk, lens_t, K, q, k, v, R,
+                                                             Hq, Hkv, D, Kin, 1e-6, 1e6, ws2,
+                                                             ws2.numel()))
+        else:
+            B_.check("qk", B_.orthrus_qk_norm_rope(qkv, wq, wk, lens_t, K, q, k, v, R, Hq, Hkv,
+                                                   D, 1e-6, 1e6))
+        outs.append((q, k, v))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def test_block_tokens_and_consensus_tokens():
     B, K = 3, 6
     anchor = torch.tensor([7, 8, 9], dtype=torch.int32, device=DEV)

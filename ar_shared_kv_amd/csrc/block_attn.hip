@@ -1152,13 +1152,18 @@ __global__ void __launch_bounds__(128 * NG) attn_merge_kernel(AttnParams p)
 // --------------------------------------------------------------------------
 // launch
 // --------------------------------------------------------------------------
-// Deepest K/V ring that fits the 160 KiB of LDS next to the page-id staging
-// (paged) or the query tile (contiguous).
+// K/V ring slots: as many as fit the 160 KiB of LDS next to the page-id
+// staging (paged) or the query tile (contiguous), at most 4.  Two tiles fly
+// ahead of the one computed (below), so a third slot is all the ring needs;
+// a power of two keeps the slot base a shift, which lets every LDS operand
+// read be one lane offset plus an immediate.  With 5 slots the compiler kept
+// one precomputed offset per read and two adds per read per tile (96 VALU
+// instructions per tile in the 256-row work-group, 40 registers, and spills).
 constexpr int ring_depth(int D, int NR, bool paged, bool qlds) {
     const int slot = 64 * D * 2 * 2;
     const int extra = paged ? kMaxSplitPages * 4 : (qlds ? 32 * NR * D * 2 : 0);
     const int n = (163840 - extra) / slot;
-    return n > 6 ? 6 : n;
+    return n > 4 ? 4 : n;
 }
 // Tiles in flight ahead of the one computed: 2 (with every CU streaming, a
 // deeper queue delays the first tiles more than it speeds up the last),

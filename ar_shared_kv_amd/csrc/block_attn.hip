@@ -190,14 +190,19 @@ attn_bf16_kernel(AttnParams p)
     constexpr int PAGE_BYTES = PAGED ? kMaxSplitPages * 4 : 0;
     constexpr int RING = FP8 ? NSTAGE * SLOT8 : NSTAGE * SLOT;
     constexpr int BF_OFF = RING;                          // FP8: two bf16 tile buffers
-    constexpr int BF_BYTES = FP8 ? 2 * SLOT : 0;
+    // FP8: two decoded tile buffers (decode of tile t+1 may start while other
+    // waves still read tile t), or one with a 2-slot ring, so that two
+    // work-groups of up to four waves share a CU (66 KiB each)
+    constexpr int FP8_BUFS = NSTAGE == 2 ? 1 : 2;
+    constexpr int BF_BYTES = FP8 ? FP8_BUFS * SLOT : 0;
     constexpr int LDS_TOTAL = RING + BF_BYTES + Q_EXTRA + PAGE_BYTES;
     __shared__ __attribute__((aligned(1024))) char smem[LDS_TOTAL];
     int* s_pages = reinterpret_cast<int*>(smem + RING + BF_BYTES + Q_EXTRA);   // PAGED only
     constexpr int Q_OFF = QSLOT ? (NSTAGE - 1) * SLOT : RING + BF_BYTES;
     // LDS of tile t's bf16 K and V (the ring slot, or FP8's decoded buffer)
     auto tile_lds = [&](int t) __attribute__((always_inline)) -> char* {
-        return FP8 ? smem + BF_OFF + (t & 1) * SLOT : smem + (t % NSTAGE) * SLOT;
+        return FP8 ? smem + BF_OFF + (FP8_BUFS == 2 ? (t & 1) * SLOT : 0)
+                   : smem + (t % NSTAGE) * SLOT;
     };
 
     const int tid = threadIdx.x;
@@ -544,7 +549,15 @@ attn_bf16_kernel(AttnParams p)
         __syncthreads();
         if constexpr (FP8) {
             if (t + NPRE < n_cache_tiles) issue(t + NPRE);
-            if (t + 1 == n_cache_tiles && t + 1 < n_tiles) issue(t + 1);   // the block tile
+            if constexpr (FP8_BUFS == 2) {
+                if (t + 1 == n_cache_tiles && t + 1 < n_tiles) issue(t + 1);   // the block tile
+            } else if (t == n_cache_tiles && t > 0) {
+                // one buffer: the block rows go in once the last cache tile
+                // has been computed (every wave is past the barrier above)
+                issue(t);
+                __builtin_amdgcn_s_waitcnt(vmcnt_encode(0));
+                __syncthreads();
+            }
             if (t < n_cache_tiles) {
                 decode(t);
                 __syncthreads();
@@ -1212,10 +1225,13 @@ template <int NR, int KS>
 static hipError_t launch_fp8(const AttnParams& p, hipStream_t st) {
     dim3 grid(p.S_grid * p.B * p.Hkv, p.row_blocks);
     dim3 block(64 * NR * KS);
+    // up to four waves: a 2-slot ring and one decoded buffer, two work-groups
+    // per CU; eight waves: a 3-slot ring, two buffers, one per CU
+    constexpr int NS = NR * KS <= 4 ? 2 : 3;
     if (p.layout == 1)
-        hipLaunchKernelGGL((attn_bf16_kernel<128, NR, KS, 3, 2, true, false, true>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<128, NR, KS, NS, NS - 1, true, false, true>), grid, block, 0, st, p);
     else
-        hipLaunchKernelGGL((attn_bf16_kernel<128, NR, KS, 3, 2, false, false, true>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((attn_bf16_kernel<128, NR, KS, NS, NS - 1, false, false, true>), grid, block, 0, st, p);
     return hipGetLastError();
 }
 
@@ -1246,7 +1262,11 @@ static hipError_t launch_bf16_d(const AttnParams& p, hipStream_t st) {
             switch (p.rows_per_wg) {
                 case 32: return launch_fp8<1, 2>(p, st);
                 case 64: return launch_fp8<2, 2>(p, st);
-                case 128: return launch_fp8<4, 2>(p, st);
+                case 128:
+                    // more contiguous work-groups than CUs: four waves, two per CU
+                    if (p.layout == 0 && (int64_t)p.S_grid * p.B * p.Hkv * p.row_blocks > 256)
+                        return launch_fp8<4, 1>(p, st);
+                    return launch_fp8<4, 2>(p, st);
                 default: return launch_fp8<8, 1>(p, st);
             }
         }

@@ -26,7 +26,11 @@ namespace {
 
 constexpr int kGemmNB = 128;                  // weight rows per work-group
 constexpr int kGemmHC = 64;                   // input columns per chunk
-constexpr int kGemmTargetWG = 512;            // split-K aims at this many work-groups
+// Split-K aims at about one work-group per CU: at the Qwen3-8B layer (R = 32)
+// the four projections took 114 us with 512 (S = 8, 16, 2, 16), 102 with 256
+// (S = 4, 8, 1, 8), 109 with 192 and 108 with 384 -- fewer partial sums and
+// longer runs per work-group win until the chip is no longer filled.
+constexpr int kGemmTargetWG = 256;
 
 __device__ __forceinline__ void g_dma16(const void* gptr, uint32_t lds_addr) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);

@@ -249,8 +249,10 @@ def test_layer_validation_codes():
     assert L.orthrus_swiglu(FAKE, FAKE, 4, 1002, None) == B.ERR_UNSUPPORTED
     # the fused projections: partial sums always written
     ew = B.orthrus_gemm_epilogue_workspace_bytes
-    assert ew(32, 4096, 4096) == 16 * 32 * 4096 * 4           # split 16 ways
-    assert ew(32, 24576, 4096) == 2 * 32 * 24576 * 4           # split 2 ways
+    assert ew(32, 4096, 4096) == 8 * 32 * 4096 * 4            # split 8 ways
+    assert ew(32, 24576, 4096) == 1 * 32 * 24576 * 4           # not split, still written
+    assert ew(32, 6144, 4096) == 4 * 32 * 6144 * 4             # split 4 ways
+    assert ew(32, 4096, 12288) == 8 * 32 * 4096 * 4           # split 8 ways
     assert ew(7, 264, 64) == 7 * 264 * 4                        # not split, still written
     assert ew(32, 4096, 100) == 0
     assert B.orthrus_gemm_workspace_bytes(7, 264, 64) == 0

@@ -21,8 +21,8 @@ def bf(shape, gen, std=1.0):
 
 
 @pytest.mark.parametrize("R,N,Kin,out", [
-    (32, 6144, 4096, "f32"),      # QKV projection, split 8 ways
-    (32, 4096, 4096, "f32"),      # output projection, split 16 ways
+    (32, 6144, 4096, "f32"),      # QKV projection, split 4 ways
+    (32, 4096, 4096, "f32"),      # output projection, split 8 ways
     (32, 24576, 4096, "f32"),     # gate/up projection
     (32, 4096, 12288, "f32"),     # down projection
     (1, 6144, 4096, "f32"),       # one row (plain decoding)
@@ -134,8 +134,8 @@ def _ws(n):
 
 
 @pytest.mark.parametrize("R,H,Kin", [
-    (32, 4096, 4096),      # output projection: split 16 ways
-    (32, 4096, 12288),     # down projection: split 16 ways
+    (32, 4096, 4096),      # output projection: split 8 ways
+    (32, 4096, 12288),     # down projection: split 8 ways
     (5, 256, 64),          # not split; one float4 group per thread, most threads idle
     (3, 8192, 128),        # two groups per thread
     (2, 16384, 64),        # four groups per thread (the largest H)

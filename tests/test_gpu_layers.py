@@ -73,6 +73,16 @@ def test_gemm_rows_do_not_depend_on_the_batch():
         B_.check("gemm", B_.orthrus_gemm(x1, wd, None, y1, 1, 6144, 4096, B_.F32, ws, ws.numel()))
         torch.cuda.synchronize()
         assert torch.equal(y1[0], y32[r])
+    # 64- and 128-row work-groups add in the same order
+    for R in (50, 100):
+        xr = torch.cat([xd, bf((R - 32, 4096), gen).to(DEV)])
+        wsr = torch.empty(B_.orthrus_gemm_workspace_bytes(R, 6144, 4096) + 16, dtype=torch.uint8,
+                          device=DEV)
+        yr = torch.empty((R, 6144), dtype=torch.float32, device=DEV)
+        B_.check("gemm", B_.orthrus_gemm(xr, wd, None, yr, R, 6144, 4096, B_.F32, wsr,
+                                         wsr.numel()))
+        torch.cuda.synchronize()
+        assert torch.equal(yr[:32], y32)
 
 
 def test_rmsnorm_swiglu_embed():

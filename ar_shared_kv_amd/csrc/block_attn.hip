@@ -139,10 +139,10 @@ __device__ __forceinline__ bool lpt_item(const AttnParams& p, int pos, int lane,
 // in two key slices, or 128 rows in one) within 256 registers per lane.
 // FP8: the cache holds OCP e4m3 codes with one power-of-two scale per (row,
 // KV head).  Cache tiles stream into the ring as codes and scales (half the
-// bytes); once a tile has landed the work-group decodes it into one of two
-// bf16 tile buffers (code x scale is exact in bf16), and the tile is then
-// computed exactly as a bf16 one.  The block rows arrive as bf16 and go
-// straight into a tile buffer.
+// bytes); once a tile has landed the work-group decodes it into a bf16 tile
+// buffer (one of two; one alone with a 2-slot ring) -- code x scale is exact
+// in bf16 -- and the tile is then computed exactly as a bf16 one.  The block
+// rows arrive as bf16 and go straight into a tile buffer.
 template <int D, int NR, int KS, int NSTAGE, int NPRE, bool PAGED, bool QLDS, bool FP8>
 __global__ void __launch_bounds__(64 * NR * KS, (NR * KS == 4 && NSTAGE == 2) ? 2 : 1)
 attn_bf16_kernel(AttnParams p)
@@ -1220,8 +1220,8 @@ static hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-// fp8 cache (head_dim 128): a 3-slot ring of codes, two tiles in flight, the
-// query in registers, one work-group per CU
+// fp8 cache (head_dim 128): the query in registers; the ring and decoded
+// buffers by wave count (below)
 template <int NR, int KS>
 static hipError_t launch_fp8(const AttnParams& p, hipStream_t st) {
     dim3 grid(p.S_grid * p.B * p.Hkv, p.row_blocks);

@@ -140,8 +140,11 @@ class Step:
         e = 2 if cfg.dtype == "bf16" else 4
         lay0 = st.layers[0]
         per_set = nl * e * sum(getattr(lay0, k).numel() for k in
-                               ("k_cache", "v_cache", "q_diff", "q_ar", "k_blk_diff",
-                                "v_blk_diff", "k_blk_ar", "v_blk_ar"))
+                               ("q_diff", "q_ar", "k_blk_diff", "v_blk_diff", "k_blk_ar",
+                                "v_blk_ar"))
+        # the cache: E4M3 codes (one byte) and one fp32 scale per row, or dtype
+        ncache = lay0.k_cache.numel() + lay0.v_cache.numel()
+        per_set += nl * (ncache + 4 * ncache // cfg.D if self.kv8 else e * ncache)
         per_set += e * (st.diff_logits.numel() + st.ar_logits.numel())
         if sets <= 0:
             sets = min(64, max(1, -(-(512 << 20) // per_set)))

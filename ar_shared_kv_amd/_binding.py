@@ -88,6 +88,8 @@ SIGNATURES = {
     "orthrus_block_tokens": (_I, [_P, _P, _I, _P, _I, _I, _P]),
     "orthrus_swiglu": (_I, [_P, _P, _I, _I, _P]),
     "orthrus_embed": (_I, [_P, _P, _P, _I, _I, _P]),
+    "orthrus_pack_weight": (_I, [_P, _I, _I, _P, _SZ, _P]),
+    "orthrus_packed_weight_bytes": (_SZ, [_I, _I]),
     "orthrus_status_string": (ctypes.c_char_p, [_I]),
     "orthrus_version": (_I, []),
 }
@@ -326,6 +328,14 @@ def orthrus_swiglu(gate_up, act, R, I, stream=None) -> int:
 
 def orthrus_embed(tokens, table, h, R, H, stream=None) -> int:
     return lib().orthrus_embed(ptr(tokens), ptr(table), ptr(h), R, H, _st(stream))
+
+
+def orthrus_pack_weight(w, N, Kin, packed, packed_bytes, stream=None) -> int:
+    return lib().orthrus_pack_weight(ptr(w), N, Kin, ptr(packed), packed_bytes, _st(stream))
+
+
+def orthrus_packed_weight_bytes(N, Kin) -> int:
+    return lib().orthrus_packed_weight_bytes(N, Kin)
 
 
 def orthrus_status_string(status: int) -> str:

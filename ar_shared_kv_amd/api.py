@@ -197,16 +197,54 @@ def argmax(logits, stream=None):
     return idx.view(logits.shape[:-1])
 
 
+class PackedWeight:
+    """A bf16 weight of N rows x Kin columns in the library's packed tile
+    layout (orthrus_pack_weight), as the projections and the LM head read it.
+    ``data`` is the flat bf16 storage (ceil(N / 128) * 128 * Kin values);
+    the object passes for a tensor in the binding's calls (``data_ptr``)."""
+
+    def __init__(self, data: torch.Tensor, N: int, Kin: int):
+        self.data, self.N, self.Kin = data, int(N), int(Kin)
+
+    @property
+    def device(self):
+        return self.data.device
+
+    def data_ptr(self) -> int:
+        return self.data.data_ptr()
+
+
+def pack_weight(w, out=None, stream=None) -> PackedWeight:
+    """Packs a row-major bf16 weight [N, Kin] for orthrus_gemm* and
+    lmhead_argmax (a one-time layout step, not part of a decode step)."""
+    _need("weight", w, dtype=torch.bfloat16)
+    if w.dim() != 2:
+        raise ValueError("weight is [N, Kin]")
+    N, Kin = w.shape
+    n = B_.orthrus_packed_weight_bytes(N, Kin)
+    if n == 0:
+        raise ValueError(f"weight [{N}, {Kin}]: Kin must be a positive multiple of 64")
+    if out is None:
+        out = torch.empty(n // 2, dtype=torch.bfloat16, device=w.device)
+    _need("out", out, dtype=torch.bfloat16, device=w.device)
+    B_.check("orthrus_pack_weight",
+             B_.orthrus_pack_weight(w, N, Kin, out, out.numel() * 2, stream))
+    return PackedWeight(out, N, Kin)
+
+
 def lmhead_argmax(hidden, weight, idx=None, workspace=None, stream=None):
-    """Greedy tokens of hidden [..., H] under the LM head weight [V, H] (bf16)."""
+    """Greedy tokens of hidden [..., H] under the LM head weight (V rows of
+    H, bf16) packed by pack_weight."""
     H = hidden.shape[-1]
     R = hidden.numel() // H
-    V = weight.shape[0]
     dt = dtype_code(hidden)
     _need("hidden", hidden)
-    if weight.dim() != 2:
-        raise ValueError("weight is [V, H]")
-    _need("weight", weight, dtype=hidden.dtype, shape=(V, H), device=hidden.device)
+    if not isinstance(weight, PackedWeight):
+        raise TypeError("weight: pack it first with pack_weight(w)")
+    if weight.Kin != H or weight.device != hidden.device:
+        raise ValueError(f"weight packs {weight.Kin} columns on {weight.device}; hidden has "
+                         f"{H} on {hidden.device}")
+    V = weight.N
     if idx is None:
         idx = torch.empty(R, dtype=torch.int32, device=hidden.device)
     _need("idx", idx, dtype=torch.int32, device=hidden.device)

@@ -16,16 +16,25 @@
 // and a second launch adds the fp32 partial sums in split order.  Every
 // output element thus goes through the same operations whatever R is: a row
 // computed in a block of 32 equals the same row computed alone.
+//
+// Weights are stored packed (pack_weight_kernel): 128 rows x 64 columns per
+// 16 KiB tile, the tiles of one 128-row block in column order, block after
+// block, rows past N zero.  A work-group's weight is then one contiguous run
+// read front to back.  Row-major rows are 2*Kin bytes apart, so every
+// work-group reading the same column chunk at once kept hitting the same HBM
+// channels: the Qwen3-8B gate/up projection (N = 24,576, Kin = 4,096) took
+// 48 us row-major and 39 us packed.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "wtile.hpp"
 
 #include "../../include/orthrus.h"
 
 namespace orthrus {
 namespace {
 
-constexpr int kGemmNB = 128;                  // weight rows per work-group
-constexpr int kGemmHC = 64;                   // input columns per chunk
+constexpr int kGemmNB = kWTileRows;           // weight rows per work-group
+constexpr int kGemmHC = kWTileCols;           // input columns per chunk (one packed tile)
 // Split-K aims at about one work-group per CU: at the Qwen3-8B layer (R = 32)
 // the four projections took 114 us with 512 (S = 8, 16, 2, 16), 102 with 256
 // (S = 4, 8, 1, 8), 109 with 192 and 108 with 384 -- fewer partial sums and
@@ -83,8 +92,9 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int 
                 const int rr = r0 + row < R ? r0 + row : R - 1;
                 src = x + (int64_t)rr * Kin + col + gsrc * 8;
             } else {
-                const int nn = n0 + row < N ? n0 + row : N - 1;
-                src = w + (int64_t)nn * Kin + col + gsrc * 8;
+                // tile (block, chunk) of the packed weight; its rows past N are zero
+                src = w + ((int64_t)blockIdx.x * (Kin / HC) + (c_lo + c)) * (kGemmNB * HC) +
+                      row * HC + gsrc * 8;
             }
             g_dma16(src, slot + (uint32_t)(k * 1024));
         }
@@ -396,12 +406,57 @@ embed_kernel(const int32_t* __restrict__ tok, const uint16_t* __restrict__ table
     for (int i = threadIdx.x; i < H; i += 256) out[i] = bf16_bits_to_f32(row[i]);
 }
 
+// ---------------------------------------------------------- weight packing
+// One thread per 16 bytes of the packed weight (8 columns of one row of one
+// tile): a coalesced write, a 16-byte read of the row-major weight, zeros for
+// the rows past N that fill the last block.
+__global__ void __launch_bounds__(256)
+pack_weight_kernel(const uint16_t* __restrict__ w, int N, int Kin, int64_t pieces,
+                   uint16_t* __restrict__ out)
+{
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= pieces) return;
+    constexpr int PPT = kWTileRows * kWTileCols / 8;          // 16-byte pieces per tile
+    const int64_t tile = p / PPT;
+    const int q = (int)(p % PPT);
+    const int cpb = Kin / kWTileCols;                          // tiles per 128-row block
+    const int64_t n = (tile / cpb) * kWTileRows + q / (kWTileCols / 8);
+    const int64_t k = (tile % cpb) * kWTileCols + (q % (kWTileCols / 8)) * 8;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (n < N) v = *(const u32x4*)(w + n * Kin + k);
+    *(u32x4*)(out + p * 8) = v;
+}
+
 }  // namespace
 }  // namespace orthrus
 
 using namespace orthrus;
 
 extern "C" {
+
+size_t orthrus_packed_weight_bytes(int N, int Kin)
+{
+    if (N < 1 || Kin < kWTileCols || Kin % kWTileCols) return 0;
+    const int64_t blocks = ((int64_t)N + kWTileRows - 1) / kWTileRows;
+    return (size_t)blocks * kWTileRows * (size_t)Kin * sizeof(uint16_t);
+}
+
+int orthrus_pack_weight(const void *w, int N, int Kin, void *packed, size_t packed_bytes,
+                        hipStream_t stream)
+{
+    if (!w || !packed) return ORTHRUS_ERR_NULL;
+    if (N < 1 || Kin < 1) return ORTHRUS_ERR_SHAPE;
+    const size_t need = orthrus_packed_weight_bytes(N, Kin);
+    if (!need) return ORTHRUS_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(w) & 15u) || (reinterpret_cast<uintptr_t>(packed) & 15u))
+        return ORTHRUS_ERR_UNSUPPORTED;
+    if (packed_bytes < need) return ORTHRUS_ERR_WORKSPACE;
+    const int64_t pieces = (int64_t)(need / 16);
+    hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0,
+                       stream, static_cast<const uint16_t *>(w), N, Kin, pieces,
+                       static_cast<uint16_t *>(packed));
+    return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
 
 namespace {
 

@@ -19,20 +19,19 @@
 // reduced over the lanes, the waves and, in a second launch with one
 // work-group per row, over the vocabulary blocks.
 //
-// HBM channels vs one summation order: weight rows are H*2 bytes apart, so
-// work-groups that all read the same column chunk at once keep hitting the
-// same HBM channels; blocks must start their walks over H at different
-// places.  To keep one fp32 summation order for every vocabulary row, H is
-// cut into NSEG segments, each summed from zero in column order, and the
-// logit is (((S_0 + S_1) + S_2) + ...) in segment order.  A block may start
-// at segment 0 or at one of the last NSLOT segments: the segments it walks
-// before wrapping around are parked in NSLOT register slots, the others are
-// added to the running total as they finish, and the parked ones last.
-// Every vocabulary row thus goes through the same fp32 operations whatever
-// block it is in: equal weight rows give bitwise-equal logits anywhere in V,
-// and ties go to the lowest index.
+// The weight is stored packed (orthrus_pack_weight: 128 x 64 tiles, a block's
+// tiles in column order, block after block), so each work-group streams one
+// contiguous 1 MiB run (H = 4,096).  Row-major rows are H*2 bytes apart and
+// work-groups reading the same column chunk at once kept hitting the same HBM
+// channels: at the Qwen3-8B head (32 rows) 268 us per call row-major, 228 us
+// with row-major walks started at nine different places (and a bookkeeping of
+// segment sums to keep one summation order), 215 us packed.  Every block
+// walks H from column 0 in order, so every vocabulary row goes through the
+// same fp32 operations: equal weight rows give bitwise-equal logits anywhere
+// in V, and ties go to the lowest index.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "wtile.hpp"
 
 #include "../../include/orthrus.h"
 
@@ -54,11 +53,10 @@ __device__ __forceinline__ void lm_dma16(const void* gptr, uint32_t lds_addr) {
                  : "memory", "m0");
 }
 
-// HC hidden columns per chunk, NSTAGE ring slots (NSTAGE - 1 chunks in flight
-// while one is computed), RB hidden rows per work-group (32, 64, 128 or 256:
-// the weight is read once per RB rows), NSEG segments of H summed apart
-// (NSEG divides H / HC), NSLOT < NSEG parked segment sums.
-template <int HC, int NSTAGE, int RB, int NSEG, int NSLOT>
+// HC hidden columns per chunk (one packed tile), NSTAGE ring slots (NSTAGE - 1
+// chunks in flight while one is computed), RB hidden rows per work-group (32,
+// 64, 128 or 256: the weight is read once per RB rows).
+template <int HC, int NSTAGE, int RB>
 __global__ void __launch_bounds__(256, 2)
 lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int R, int H,
                      int V, int nvb, uint64_t* __restrict__ ws)
@@ -71,6 +69,7 @@ lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict_
     constexpr int RPP = 1024 / (HC * 2);        // rows per 1 KiB wave load
     constexpr int LOADS = SLOT / 4096;          // loads per lane per chunk
     constexpr int NPRE = NSTAGE - 1;
+    static_assert(HC == kWTileCols && kLmVB == kWTileRows, "one packed tile per chunk");
     static_assert(SLOT % 4096 == 0 && WB % 1024 == 0, "whole wave loads per chunk");
     static_assert(LOADS * NSTAGE <= 63, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * SLOT];
@@ -83,21 +82,15 @@ lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict_
     const int v0 = vb * kLmVB;
     const int r0 = blockIdx.y * RB;
     const int nchunk = H / HC;
-    const int seg_len = nchunk / NSEG;           // chunks per segment
-    // the walk starts at segment 0 or at one of the last NSLOT segments, by
-    // block, and wraps around H
-    const int ph = NSLOT > 0 ? vb % (NSLOT + 1) : 0;
-    const int s0 = ph == 0 ? 0 : NSEG - ph;
+    const uint16_t* wblk = w + (int64_t)vb * nchunk * (kLmVB * HC);   // this block's tiles
     const uint32_t lds_base = (uint32_t)(uintptr_t)(ORTHRUS_LDS void*)&smem[0];
 
-    // DMA of the c-th chunk of the walk into slot c % NSTAGE.  A 1 KiB wave load covers RPP rows
+    // DMA of chunk c into slot c % NSTAGE.  A 1 KiB wave load covers RPP rows
     // of GR granules; lane l writes LDS granule l % GR of its row with the
     // global granule (l % GR) ^ (row % GR), so that granule g of a row sits at
     // g ^ (row % GR) and the fragment reads below spread over the banks.
     auto issue = [&](int c) __attribute__((always_inline)) {
         const uint32_t slot = lds_base + (uint32_t)((c % NSTAGE) * SLOT);
-        const int sg = s0 + c / seg_len;
-        const int col = ((sg < NSEG ? sg : sg - NSEG) * seg_len + c % seg_len) * HC;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int k = i * 4 + wave;                  // 1 KiB piece of the slot
@@ -107,10 +100,9 @@ lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict_
             const uint16_t* src;
             if (isx) {
                 const int rr = r0 + row < R ? r0 + row : R - 1;
-                src = x + (int64_t)rr * H + col + gsrc * 8;
+                src = x + (int64_t)rr * H + c * HC + gsrc * 8;
             } else {
-                const int vv = v0 + row < V ? v0 + row : V - 1;
-                src = w + (int64_t)vv * H + col + gsrc * 8;
+                src = wblk + (int64_t)c * (kLmVB * HC) + row * HC + gsrc * 8;
             }
             lm_dma16(src, slot + (uint32_t)(k * 1024));
         }
@@ -129,16 +121,9 @@ lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict_
     };
     static_assert(NPRE - 1 <= 3, "wait_chunk covers up to 3 later chunks");
 
-    constexpr int NP = NSLOT > 0 ? NSLOT : 1;
-    f32x16 park[NP][NB];      // sums of segments NSEG-NSLOT.. walked before the wrap
-    f32x16 tot[NB];           // S_0 + S_1 + ... in segment order
-    f32x16 cur[NB];           // the segment being walked, summed from zero
+    f32x16 tot[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) cur[j] = tot[j] = f32x16{};
-#pragma unroll
-    for (int k = 0; k < NP; ++k)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) park[k][j] = f32x16{};
+    for (int j = 0; j < NB; ++j) tot[j] = f32x16{};
     const int vrow = wave * 32 + (lane & 31);            // this lane's vocabulary row (A operand)
     for (int c = 0; c < NPRE && c < nchunk; ++c) issue(c);
     for (int c = 0; c < nchunk; ++c) {
@@ -162,39 +147,9 @@ lmhead_argmax_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict_
         for (int ds = 0; ds < HC / 16; ++ds)
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                cur[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                tot[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, af[ds]), __builtin_bit_cast(bf16x8, bfr[j][ds]),
-                    cur[j], 0, 0, 0);
-        if (c % seg_len == seg_len - 1) {      // segment done (a wave-uniform branch)
-            const int sg = s0 + c / seg_len;
-            const int seg = sg < NSEG ? sg : sg - NSEG;
-            const bool parked = s0 > 0 && seg >= s0;     // walked before the wrap
-#pragma unroll
-            for (int k = 0; k < NP; ++k) {
-                const bool here = parked && seg == NSEG - NSLOT + k;
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) park[k][j][e] = here ? cur[j][e] : park[k][j][e];
-            }
-            const bool first = !parked && seg == 0;      // tot = S_0, then tot + S_seg
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    tot[j][e] = parked ? tot[j][e] : (first ? cur[j][e] : tot[j][e] + cur[j][e]);
-#pragma unroll
-            for (int j = 0; j < NB; ++j) cur[j] = f32x16{};
-        }
-    }
-    // the parked segments, in segment order: the same additions for every block
-#pragma unroll
-    for (int k = 0; k < NP; ++k) {
-        const bool used = s0 > 0 && NSEG - NSLOT + k >= s0;
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) tot[j][e] = used ? tot[j][e] + park[k][j][e] : tot[j][e];
+                    tot[j], 0, 0, 0);
     }
 
     // tot[j][i] = logit of vocabulary row v0 + 32*wave + 8*(i/4) + 4*half + i%4
@@ -250,23 +205,6 @@ lmhead_finalize_kernel(const uint64_t* __restrict__ ws, int nvb, int32_t* __rest
     }
 }
 
-// Launch with NSEG segments (or the largest power of two below it that
-// divides the H chunks) and NSLOT parked sums (fewer with fewer segments).
-template <int NSTAGE, int RB, int NSEG, int NSLOT>
-void launch_lm_seg(int nchunk, dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w,
-                   int R, int H, int V, int nvb, uint64_t* ws)
-{
-    if constexpr (NSEG > 1) {
-        if (nchunk % NSEG != 0) {
-            constexpr int NS2 = NSEG / 2;
-            constexpr int NL2 = NSLOT < NS2 ? NSLOT : NS2 - 1;
-            return launch_lm_seg<NSTAGE, RB, NS2, NL2>(nchunk, grid, st, x, w, R, H, V, nvb, ws);
-        }
-    }
-    hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, NSTAGE, RB, NSEG, NSLOT>), grid, dim3(256), 0,
-                       st, x, w, R, H, V, nvb, ws);
-}
-
 int64_t lm_blocks(int V) { return ((int64_t)V + kLmVB - 1) / kLmVB; }
 
 bool lm_shape_ok(int R, int H, int V) {
@@ -306,29 +244,25 @@ int orthrus_lmhead_argmax(const void *hidden, const void *weight, int R, int H, 
     // hidden rows per work-group: the weight is read ceil(R / RB) times
     const uint16_t *xp = static_cast<const uint16_t *>(hidden);
     const uint16_t *wp = static_cast<const uint16_t *>(weight);
-    const int nchunk = H / kLmHC;
+    const dim3 g1((unsigned)nvb, 1);
     if (R <= 32) {
-        // 16 segments, 8 parked: 9 start phases 512 bytes apart.  Qwen3-8B head
-        // (H = 4,096, 32 rows), us per call: one phase 267, 8 phases 1 KiB
-        // apart 244, 9 phases 256 B apart 251, 9 phases 128 B apart 376
-        // (per-chunk segment sums cost more than they spread), this 228
-        launch_lm_seg<kLmStages, 32, 16, 8>(nchunk, dim3((unsigned)nvb, 1), stream, xp, wp, R, H,
-                                            V, (int)nvb, ws);
+        hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, kLmStages, 32>), g1, dim3(256), 0, stream,
+                           xp, wp, R, H, V, (int)nvb, ws);
     } else if (R <= 64) {
-        launch_lm_seg<kLmStages, 64, 4, 3>(nchunk, dim3((unsigned)nvb, 1), stream, xp, wp, R, H, V,
-                                        (int)nvb, ws);
+        hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, kLmStages, 64>), g1, dim3(256), 0, stream,
+                           xp, wp, R, H, V, (int)nvb, ws);
     } else if (R > 128) {
         // one work-group per CU (104 KiB of LDS), half the weight reads of
-        // 128-row blocks (R = 1024: 1.70 vs 1.91 ms per call); no registers
-        // left for segment sums
-        hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, 2, 256, 1, 0>),
+        // 128-row blocks (R = 1024: 1.70 vs 1.91 ms per call, row-major weight)
+        hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, 2, 256>),
                            dim3((unsigned)nvb, (unsigned)((R + 255) / 256)), dim3(256), 0, stream,
                            xp, wp, R, H, V, (int)nvb, ws);
     } else {
         // two slots: two work-groups per CU (68 KiB of LDS each) beat one with
-        // three slots (R = 1024: 1.90 vs 2.13 ms per call)
-        launch_lm_seg<2, 128, 2, 1>(nchunk, dim3((unsigned)nvb, (unsigned)((R + 127) / 128)), stream,
-                                 xp, wp, R, H, V, (int)nvb, ws);
+        // three slots (R = 1024: 1.90 vs 2.13 ms per call, row-major weight)
+        hipLaunchKernelGGL((lmhead_argmax_kernel<kLmHC, 2, 128>),
+                           dim3((unsigned)nvb, (unsigned)((R + 127) / 128)), dim3(256), 0, stream,
+                           xp, wp, R, H, V, (int)nvb, ws);
     }
     if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
     hipLaunchKernelGGL(lmhead_finalize_kernel, dim3((unsigned)R), dim3(256), 0, stream,

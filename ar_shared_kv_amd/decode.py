@@ -47,6 +47,9 @@ def _ok(fn, st):
 PREFILL_CHUNK = 64
 
 
+_PACKED = (".wqkv", ".wo", ".wgu", ".wdown", "lm_head")
+
+
 class DecodeModel:
     """Weights on the GPU plus per-batch buffers.  The row buffers hold a
     block of B x max(K, PREFILL_CHUNK) rows: a decode block, or one prefill
@@ -55,7 +58,12 @@ class DecodeModel:
     def __init__(self, dims: Dims, weights: dict, B: int, K: int, cap: int, device="cuda"):
         self.d, self.B, self.K, self.cap = dims, B, K, cap
         dev = torch.device(device)
-        self.w = {k: v.to(dev).contiguous() for k, v in weights.items()}
+        # the projection and LM-head matrices in the packed tile layout the
+        # weight-streaming kernels read (packed once, here)
+        self.w = {}
+        for k, v in weights.items():
+            t = v.to(dev).contiguous()
+            self.w[k] = api.pack_weight(t) if k.endswith(_PACKED) else t
         d = dims
         self.mask_token = d.V                      # the extra embedding row
         R = B * max(K, PREFILL_CHUNK)              # rows of the largest block

@@ -44,7 +44,8 @@ HBM_PEAK_GBPS = 8000.0
 ATTN_SOURCES = ("ar_shared_kv_amd/csrc/block_attn.hip", "ar_shared_kv_amd/csrc/kernels.hpp",
                 "ar_shared_kv_amd/csrc/common.hpp", "ar_shared_kv_amd/csrc/abi.cpp")
 # ... and what the fused LM-head argmax call does
-LM_SOURCES = ("ar_shared_kv_amd/csrc/lmhead.hip", "ar_shared_kv_amd/csrc/common.hpp")
+LM_SOURCES = ("ar_shared_kv_amd/csrc/lmhead.hip", "ar_shared_kv_amd/csrc/common.hpp",
+              "ar_shared_kv_amd/csrc/wtile.hpp")
 
 
 def attn_source_hash(sources=ATTN_SOURCES):
@@ -459,7 +460,7 @@ def lmhead_main(args):
     R, H, V = args.lmhead_rows, 4096, 151936
     calibrate(args.calib_bytes)
     h, w = W.lmhead_inputs(R, H, V, seed=0)
-    hd, wd = h.cuda(), w.cuda()
+    hd, wd = h.cuda(), api.pack_weight(w.cuda())     # the layout step, untimed
     idx = torch.empty(R, dtype=torch.int32, device="cuda")
     n = B_.orthrus_lmhead_argmax_workspace_bytes(R, H, V, B_.BF16)
     ws = torch.empty(n, dtype=torch.uint8, device="cuda")

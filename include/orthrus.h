@@ -281,7 +281,8 @@ size_t orthrus_argmax_workspace_bytes(int64_t rows, int V, int dtype);
  *
  *  hidden    [R][H] bf16, 16-byte aligned (final hidden states of R rows,
  *            e.g. the B*K block rows of one view)
- *  weight    [V][H] bf16, 16-byte aligned (the LM head, one row per token)
+ *  weight    the LM head ([V][H] bf16, one row per token) in the packed tile
+ *            layout of orthrus_pack_weight(weight, V, H, ...), 16-byte aligned
  *  idx       out int32 [R]
  *  workspace >= orthrus_lmhead_argmax_workspace_bytes(R, H, V, dtype) bytes
  *            (8-byte aligned); contents on entry are ignored.
@@ -362,9 +363,30 @@ int orthrus_stream_read(const void *src, size_t bytes, int work_groups,
  */
 
 /*
+ * orthrus_pack_weight -- lays a weight out for the projections and the LM
+ * head: w bf16 [N][Kin] row-major (16-byte aligned) is written to packed as
+ * tiles of 128 rows x 64 columns (16 KiB each, rows in order, 128 bytes per
+ * row); the tiles of one 128-row block follow each other in column order, and
+ * the blocks follow each other: element (n, k) lands at bf16 index
+ * ((n / 128) * (Kin / 64) + k / 64) * 8192 + (n % 128) * 64 + k % 64.  The
+ * rows of the last block past N are zero.  Each work-group of a projection
+ * or of the LM head then reads its weight as one contiguous run instead of
+ * rows 2*Kin bytes apart that keep landing on the same HBM channels.  A
+ * load-time step: weights are packed once and used by every decode step.
+ *  Kin a multiple of 64; packed (16-byte aligned, not overlapping w) holds
+ *  orthrus_packed_weight_bytes(N, Kin) bytes, else ORTHRUS_ERR_WORKSPACE.
+ */
+int orthrus_pack_weight(const void *w, int N, int Kin, void *packed,
+                        size_t packed_bytes, hipStream_t stream);
+/* ceil(N / 128) * 128 * Kin * 2 bytes; 0 if N < 1 or Kin is not a positive
+ * multiple of 64. */
+size_t orthrus_packed_weight_bytes(int N, int Kin);
+
+/*
  * orthrus_gemm -- y = x W^T (+ residual): x bf16 [R][Kin], W bf16 [N][Kin]
- * (a linear layer's weight, one row per output), residual fp32 [R][N] or
- * NULL, y [R][N] in out_dtype (F32 or BF16; y may be the residual itself).
+ * (a linear layer's weight, one row per output) in the packed tile layout of
+ * orthrus_pack_weight, residual fp32 [R][N] or NULL, y [R][N] in out_dtype
+ * (F32 or BF16; y may be the residual itself).
  * fp32 accumulation in a fixed order per output that does not depend on R
  * (the input dimension is split S ways by N and Kin only; the partial sums
  * are added in split order).  Kin a multiple of 64, N a multiple of 4,
@@ -391,7 +413,8 @@ int orthrus_rmsnorm(const float *x, const void *weight, void *y, int R, int H,
  * write the partial sums (also when the input dimension is not split), so
  * workspace >= orthrus_gemm_epilogue_workspace_bytes(R, N, Kin) bytes,
  * 16-byte aligned, with N the projection's output width.  Same x / W
- * contract as orthrus_gemm (Kin a multiple of 64, 16-byte aligned).
+ * contract as orthrus_gemm (W packed by orthrus_pack_weight, Kin a multiple
+ * of 64, 16-byte aligned).
  */
 size_t orthrus_gemm_epilogue_workspace_bytes(int R, int N, int Kin);
 

@@ -288,6 +288,24 @@ def test_layer_validation_codes():
     assert qk(*bad) == B.ERR_WORKSPACE
 
 
+def test_pack_weight_sizes_and_validation():
+    pb = B.orthrus_packed_weight_bytes
+    assert pb(6144, 4096) == 6144 * 4096 * 2                   # whole 128-row blocks
+    assert pb(151936, 4096) == 1187 * 128 * 4096 * 2           # the Qwen3 vocabulary: 1,187 blocks
+    assert pb(132, 64) == 256 * 64 * 2                          # ragged: padded to 256 rows
+    assert pb(1, 192) == 128 * 192 * 2
+    assert pb(0, 64) == 0 and pb(128, 0) == 0 and pb(128, 100) == 0 and pb(128, 32) == 0
+    P = B.lib().orthrus_pack_weight
+    need = pb(132, 64)
+    assert P(None, 132, 64, FAKE, need, None) == B.ERR_NULL
+    assert P(FAKE, 132, 64, None, need, None) == B.ERR_NULL
+    assert P(FAKE, 0, 64, FAKE, need, None) == B.ERR_SHAPE
+    assert P(FAKE, 132, 100, FAKE, need, None) == B.ERR_UNSUPPORTED   # Kin not a multiple of 64
+    assert P(FAKE + 8, 132, 64, FAKE, need, None) == B.ERR_UNSUPPORTED
+    assert P(FAKE, 132, 64, FAKE + 8, need, None) == B.ERR_UNSUPPORTED
+    assert P(FAKE, 132, 64, FAKE, need - 2, None) == B.ERR_WORKSPACE
+
+
 def test_single_hip_runtime_in_process():
     import torch  # noqa: F401
     B.lib()

@@ -9,6 +9,7 @@ import torch
 
 import oracle
 from ar_shared_kv_amd import _binding as B_
+from ar_shared_kv_amd import api
 from gpu_util import record, say
 from oracle import model as M
 
@@ -39,7 +40,7 @@ def test_gemm_matches_fp64(R, N, Kin, out):
     bound = 1.01 * Kin * 2.0 ** -24 * mag + 2.0 ** -23 * np.abs(ref)
     if out == "bf16":
         bound = bound + 2.0 ** -8 * np.abs(ref)
-    xd, wd, rd = x.to(DEV), w.to(DEV), res.to(DEV)
+    xd, wd, rd = x.to(DEV), api.pack_weight(w.to(DEV)), res.to(DEV)
     y = torch.empty((R, N), dtype=torch.float32 if out == "f32" else torch.bfloat16, device=DEV)
     n = B_.orthrus_gemm_workspace_bytes(R, N, Kin)
     ws = torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
@@ -59,10 +60,28 @@ def test_gemm_matches_fp64(R, N, Kin, out):
         assert torch.equal(y2, y)
 
 
+@pytest.mark.parametrize("N,Kin", [(6144, 4096), (132, 64), (1, 192), (300, 128)])
+def test_pack_weight_is_the_tile_permutation(N, Kin):
+    """The packed layout is a pure rearrangement: tile (block, chunk) holds
+    rows 128*block.. and columns 64*chunk.. in row order, blocks padded with
+    zero rows; checked bit for bit against a numpy reshape of the weight."""
+    gen = torch.Generator().manual_seed(N + Kin)
+    w = bf((N, Kin), gen)
+    pw = api.pack_weight(w.to(DEV))
+    torch.cuda.synchronize()
+    nb = (N + 127) // 128
+    assert pw.data.numel() * 2 == B_.orthrus_packed_weight_bytes(N, Kin) == nb * 128 * Kin * 2
+    wp = np.zeros((nb * 128, Kin), np.uint16)
+    wp[:N] = w.view(torch.int16).numpy().view(np.uint16)
+    ref = wp.reshape(nb, 128, Kin // 64, 64).transpose(0, 2, 1, 3).reshape(-1)
+    got = pw.data.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
 def test_gemm_rows_do_not_depend_on_the_batch():
     gen = torch.Generator().manual_seed(3)
     x, w = bf((32, 4096), gen), bf((6144, 4096), gen, 4096 ** -0.5)
-    xd, wd = x.to(DEV), w.to(DEV)
+    xd, wd = x.to(DEV), api.pack_weight(w.to(DEV))
     ws = torch.empty(B_.orthrus_gemm_workspace_bytes(32, 6144, 4096) + 16, dtype=torch.uint8,
                      device=DEV)
     y32 = torch.empty((32, 6144), dtype=torch.float32, device=DEV)
@@ -152,7 +171,7 @@ def _ws(n):
 ])
 def test_gemm_rmsnorm_equals_gemm_then_rmsnorm(R, H, Kin):
     gen = torch.Generator().manual_seed(R * 13 + H + Kin)
-    x, w = bf((R, Kin), gen).to(DEV), bf((H, Kin), gen, Kin ** -0.5).to(DEV)
+    x, w = bf((R, Kin), gen).to(DEV), api.pack_weight(bf((H, Kin), gen, Kin ** -0.5).to(DEV))
     nw = bf((H,), gen).to(DEV)
     h0 = (torch.randn((R, H), generator=gen) * 2).to(DEV)
     say(f"gemm_rmsnorm R={R} H={H} Kin={Kin}")
@@ -176,7 +195,7 @@ def test_gemm_rmsnorm_equals_gemm_then_rmsnorm(R, H, Kin):
 @pytest.mark.parametrize("R,I,Kin", [(32, 12288, 4096), (7, 132, 64), (40, 1024, 512)])
 def test_gemm_swiglu_equals_gemm_then_swiglu(R, I, Kin):
     gen = torch.Generator().manual_seed(R + I + Kin)
-    x, w = bf((R, Kin), gen).to(DEV), bf((2 * I, Kin), gen, Kin ** -0.5).to(DEV)
+    x, w = bf((R, Kin), gen).to(DEV), api.pack_weight(bf((2 * I, Kin), gen, Kin ** -0.5).to(DEV))
     say(f"gemm_swiglu R={R} I={I} Kin={Kin}")
     gu = torch.empty((R, 2 * I), dtype=torch.float32, device=DEV)
     ws = _ws(B_.orthrus_gemm_workspace_bytes(R, 2 * I, Kin))
@@ -195,7 +214,7 @@ def test_gemm_qk_norm_rope_equals_gemm_then_qk_norm_rope(B, K, Kin, lens):
     gen = torch.Generator().manual_seed(B * 100 + K)
     Hq, Hkv, D = 32, 8, 128
     R, N = B * K, (Hq + 2 * Hkv) * D
-    x, w = bf((R, Kin), gen).to(DEV), bf((N, Kin), gen, Kin ** -0.5).to(DEV)
+    x, w = bf((R, Kin), gen).to(DEV), api.pack_weight(bf((N, Kin), gen, Kin ** -0.5).to(DEV))
     wq, wk = bf((D,), gen).to(DEV), bf((D,), gen).to(DEV)
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
     say(f"gemm_qk_norm_rope B={B} K={K} Kin={Kin}")

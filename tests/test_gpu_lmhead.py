@@ -56,32 +56,32 @@ def test_lmhead_argmax_matches_oracle(case):
     name, R, H, V = case
     h, w = W.lmhead_inputs(R, H, V, seed=R)
     say(f"lmhead {name} R={R} H={H} V={V}")
-    got = api.lmhead_argmax(h.cuda(), w.cuda()).cpu().numpy()
+    got = api.lmhead_argmax(h.cuda(), api.pack_weight(w.cuda())).cpu().numpy()
     exact = check(name, h, w, got)
     assert exact >= R // 2
 
 
 @pytest.mark.parametrize("R,H,rows", [
-    (4, 512, (2900, 333)),          # 32-row blocks, 8 segments; different blocks and segments
+    (4, 512, (2900, 333)),          # 32-row work-groups; vocabulary blocks 22 and 2
     (4, 512, (380, 333)),           # same block, different waves
-    (50, 512, (2177, 1)),           # 64-row blocks, 4 segments (blocks 17 and 0)
-    (100, 512, (1999, 5)),          # 128-row blocks, 2 segments (blocks 15 and 0)
-    (300, 512, (4001, 7)),          # 256-row blocks, one segment
+    (50, 512, (2177, 1)),           # 64-row work-groups (blocks 17 and 0)
+    (100, 512, (1999, 5)),          # 128-row work-groups (blocks 15 and 0)
+    (300, 512, (4001, 7)),          # 256-row work-groups
     (32, 4096, (151935, 77777)),    # the Qwen3-8B head: the last row and one far away
 ])
 def test_lmhead_argmax_duplicate_rows_take_the_lowest_index(R, H, rows):
     V = max(rows) + 1 if max(rows) + 1 > 3000 else 3000
     h, w = W.lmhead_inputs(R, H, V, seed=11)
-    # two weight rows in different vocabulary blocks (each block starts its
-    # walk over H at another segment) are the same vector, aligned with
-    # hidden row 0: for row 0 they must carry bitwise-equal fp32 logits, the
-    # largest of the row, and the lower index wins
+    # two weight rows (in different vocabulary blocks but one) are the same
+    # vector, aligned with hidden row 0: for row 0 they must carry
+    # bitwise-equal fp32 logits, the largest of the row, and the lower index
+    # wins
     best = (h[0].float() / h[0].float().norm()).to(torch.bfloat16)
     hi, lo = rows
     w[hi] = best
     w[lo] = best
     say(f"lmhead duplicates R={R} H={H} rows={rows}")
-    got = api.lmhead_argmax(h.cuda(), w.cuda()).cpu().numpy()
+    got = api.lmhead_argmax(h.cuda(), api.pack_weight(w.cuda())).cpu().numpy()
     record("lmhead-ties", f"R={R} H={H} rows {hi}/{lo}", token=int(got[0]), expected=int(lo))
     assert got[0] == lo
     check("duplicates", h, w, got)
@@ -90,7 +90,7 @@ def test_lmhead_argmax_duplicate_rows_take_the_lowest_index(R, H, rows):
 def test_lmhead_argmax_graph_replay_equals_eager():
     R, H, V = 32, 1024, 20000
     h, w = W.lmhead_inputs(R, H, V, seed=5)
-    hd, wd = h.cuda(), w.cuda()
+    hd, wd = h.cuda(), api.pack_weight(w.cuda())
     idx = torch.empty(R, dtype=torch.int32, device="cuda")
     from ar_shared_kv_amd import _binding as B_
     n = B_.orthrus_lmhead_argmax_workspace_bytes(R, H, V, B_.BF16)

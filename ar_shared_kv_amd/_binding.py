@@ -90,6 +90,7 @@ SIGNATURES = {
     "orthrus_embed": (_I, [_P, _P, _P, _I, _I, _P]),
     "orthrus_pack_weight": (_I, [_P, _I, _I, _P, _SZ, _P]),
     "orthrus_packed_weight_bytes": (_SZ, [_I, _I]),
+    "orthrus_pack_weight_gate_up": (_I, [_P, _I, _I, _P, _SZ, _P]),
     "orthrus_status_string": (ctypes.c_char_p, [_I]),
     "orthrus_version": (_I, []),
 }
@@ -332,6 +333,11 @@ def orthrus_embed(tokens, table, h, R, H, stream=None) -> int:
 
 def orthrus_pack_weight(w, N, Kin, packed, packed_bytes, stream=None) -> int:
     return lib().orthrus_pack_weight(ptr(w), N, Kin, ptr(packed), packed_bytes, _st(stream))
+
+
+def orthrus_pack_weight_gate_up(w, I, Kin, packed, packed_bytes, stream=None) -> int:
+    return lib().orthrus_pack_weight_gate_up(ptr(w), I, Kin, ptr(packed), packed_bytes,
+                                             _st(stream))
 
 
 def orthrus_packed_weight_bytes(N, Kin) -> int:

@@ -203,8 +203,8 @@ class PackedWeight:
     ``data`` is the flat bf16 storage (ceil(N / 128) * 128 * Kin values);
     the object passes for a tensor in the binding's calls (``data_ptr``)."""
 
-    def __init__(self, data: torch.Tensor, N: int, Kin: int):
-        self.data, self.N, self.Kin = data, int(N), int(Kin)
+    def __init__(self, data: torch.Tensor, N: int, Kin: int, gate_up: bool = False):
+        self.data, self.N, self.Kin, self.gate_up = data, int(N), int(Kin), gate_up
 
     @property
     def device(self):
@@ -232,6 +232,24 @@ def pack_weight(w, out=None, stream=None) -> PackedWeight:
     return PackedWeight(out, N, Kin)
 
 
+def pack_weight_gate_up(w, out=None, stream=None) -> PackedWeight:
+    """Packs the MLP's gate/up weight [2I, Kin] (gate rows, then up rows) in
+    the paired order orthrus_gemm_swiglu reads."""
+    _need("weight", w, dtype=torch.bfloat16)
+    if w.dim() != 2 or w.shape[0] % 8:
+        raise ValueError("gate/up weight is [2I, Kin] with I a multiple of 4")
+    N, Kin = w.shape
+    n = B_.orthrus_packed_weight_bytes(N, Kin)
+    if n == 0:
+        raise ValueError(f"weight [{N}, {Kin}]: Kin must be a positive multiple of 64")
+    if out is None:
+        out = torch.empty(n // 2, dtype=torch.bfloat16, device=w.device)
+    _need("out", out, dtype=torch.bfloat16, device=w.device)
+    B_.check("orthrus_pack_weight_gate_up",
+             B_.orthrus_pack_weight_gate_up(w, N // 2, Kin, out, out.numel() * 2, stream))
+    return PackedWeight(out, N, Kin, gate_up=True)
+
+
 def lmhead_argmax(hidden, weight, idx=None, workspace=None, stream=None):
     """Greedy tokens of hidden [..., H] under the LM head weight (V rows of
     H, bf16) packed by pack_weight."""
@@ -239,7 +257,7 @@ def lmhead_argmax(hidden, weight, idx=None, workspace=None, stream=None):
     R = hidden.numel() // H
     dt = dtype_code(hidden)
     _need("hidden", hidden)
-    if not isinstance(weight, PackedWeight):
+    if not isinstance(weight, PackedWeight) or weight.gate_up:
         raise TypeError("weight: pack it first with pack_weight(w)")
     if weight.Kin != H or weight.device != hidden.device:
         raise ValueError(f"weight packs {weight.Kin} columns on {weight.device}; hidden has "

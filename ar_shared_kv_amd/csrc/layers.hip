@@ -49,8 +49,14 @@ __device__ __forceinline__ void g_dma16(const void* gptr, uint32_t lds_addr) {
                  : "memory", "m0");
 }
 
+// silu(g) * u with silu(g) = g / (1 + e^-g): the one SwiGLU expression of
+// every kernel below that applies it.
+__device__ __forceinline__ float swiglu1(float g, float u) { return g / (1.f + expf(-g)) * u; }
+
 // out_mode: 0 fp32 partial (split s of S) to part[s][R][N]; 1 fp32 y (+ res);
-// 2 bf16 y (+ res)
+// 2 bf16 y (+ res); 3 SwiGLU of a paired gate/up weight (S = 1): every 8
+// weight rows are 4 gate rows then the 4 matching up rows (pack_weight_kernel
+// with pair_I), y = act bf16 [R][N / 2]
 template <int NSTAGE, int RB>
 __global__ void __launch_bounds__(256, 2)
 gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int R, int N, int Kin,
@@ -142,6 +148,33 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int 
     }
     // acc[j][i]: weight row n0 + 32*wave + 8*(i/4) + 4*half + i%4, hidden row
     // r0 + 32*j + lane%32; four consecutive outputs per store
+    if (out_mode == 3) {
+        // the block's RB x 128 fp32 results through LDS (the ring is free once
+        // every wave is past its last chunk), then one thread per (hidden row,
+        // 4 outputs): gate at paired columns 8g..8g+3, up at 8g+4..8g+7
+        __syncthreads();
+        float* buf = reinterpret_cast<float*>(smem);
+        static_assert(RB * kGemmNB * 4 <= NSTAGE * SLOT, "epilogue buffer fits in the ring");
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                *(f32x4*)(buf + (32 * j + (lane & 31)) * kGemmNB + wave * 32 + 8 * q4 + 4 * half) =
+                    f32x4{acc[j][4 * q4], acc[j][4 * q4 + 1], acc[j][4 * q4 + 2], acc[j][4 * q4 + 3]};
+        __syncthreads();
+        const int I = N / 2;
+        for (int it = tid; it < RB * (kGemmNB / 8); it += 256) {
+            const int rr = it / (kGemmNB / 8), g = it % (kGemmNB / 8);
+            const int r = r0 + rr, i = blockIdx.x * (kGemmNB / 2) + 4 * g;
+            if (r >= R || i >= I) continue;
+            const f32x4 gv = *(const f32x4*)(buf + rr * kGemmNB + 8 * g);
+            const f32x4 uv = *(const f32x4*)(buf + rr * kGemmNB + 8 * g + 4);
+            *(u32x2*)((uint16_t*)y + (int64_t)r * I + i) =
+                u32x2{pack_bf16x2(swiglu1(gv[0], uv[0]), swiglu1(gv[1], uv[1])),
+                      pack_bf16x2(swiglu1(gv[2], uv[2]), swiglu1(gv[3], uv[3]))};
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         const int r = r0 + 32 * j + (lane & 31);
@@ -364,9 +397,12 @@ qk_norm_rope_kernel(const float* __restrict__ qkv, int S, const uint16_t* __rest
 // act[r][i] = silu(g) * u, g = gu[r][i], u = gu[r][I + i], silu(g) =
 // g / (1 + e^-g); gu holds S >= 1 partial sums [S][R][2I] of the gate/up
 // projection (S = 1: the projection itself), added in split order first.
+// paired: the columns come from a paired weight (4 gate columns, then their 4
+// up columns), so g = gu[r][8(i/4) + i%4] and u = gu[r][8(i/4) + 4 + i%4].
 // One thread per four consecutive i (I a multiple of 4).
 __global__ void __launch_bounds__(256)
-swiglu_kernel(const float* __restrict__ gu, int S, uint16_t* __restrict__ act, int R, int I)
+swiglu_kernel(const float* __restrict__ gu, int S, uint16_t* __restrict__ act, int R, int I,
+              int paired)
 {
     const int I4 = I / 4;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -374,12 +410,12 @@ swiglu_kernel(const float* __restrict__ gu, int S, uint16_t* __restrict__ act, i
     const int64_t r = t / I4;
     const int i = (int)(t % I4) * 4;
     const int64_t stride = (int64_t)R * 2 * I;
-    const f32x4 g = sum_splits(gu, S, stride, r * 2 * I + i);
-    const f32x4 u = sum_splits(gu, S, stride, r * 2 * I + I + i);
-    float a[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) a[c] = g[c] / (1.f + expf(-g[c])) * u[c];
-    *(u32x2*)(act + r * I + i) = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+    const int64_t go = r * 2 * I + (paired ? 2 * i : i);
+    const int64_t uo = paired ? go + 4 : go + I;
+    const f32x4 g = sum_splits(gu, S, stride, go);
+    const f32x4 u = sum_splits(gu, S, stride, uo);
+    *(u32x2*)(act + r * I + i) = u32x2{pack_bf16x2(swiglu1(g[0], u[0]), swiglu1(g[1], u[1])),
+                                       pack_bf16x2(swiglu1(g[2], u[2]), swiglu1(g[3], u[3]))};
 }
 
 // ----------------------------------------------------- block input tokens
@@ -409,10 +445,12 @@ embed_kernel(const int32_t* __restrict__ tok, const uint16_t* __restrict__ table
 // ---------------------------------------------------------- weight packing
 // One thread per 16 bytes of the packed weight (8 columns of one row of one
 // tile): a coalesced write, a 16-byte read of the row-major weight, zeros for
-// the rows past N that fill the last block.
+// the rows past N that fill the last block.  pair_I > 0: the weight is a
+// gate/up pair [2I][Kin] (gate rows, then up rows) and packed row n holds, in
+// every group of 8, gate rows 4(n/8)..+3 and then the matching up rows.
 __global__ void __launch_bounds__(256)
 pack_weight_kernel(const uint16_t* __restrict__ w, int N, int Kin, int64_t pieces,
-                   uint16_t* __restrict__ out)
+                   int pair_I, uint16_t* __restrict__ out)
 {
     const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (p >= pieces) return;
@@ -422,8 +460,10 @@ pack_weight_kernel(const uint16_t* __restrict__ w, int N, int Kin, int64_t piece
     const int cpb = Kin / kWTileCols;                          // tiles per 128-row block
     const int64_t n = (tile / cpb) * kWTileRows + q / (kWTileCols / 8);
     const int64_t k = (tile % cpb) * kWTileCols + (q % (kWTileCols / 8)) * 8;
+    const int64_t src = pair_I > 0 ? (n % 8 < 4 ? 4 * (n / 8) + n % 8 : pair_I + 4 * (n / 8) + n % 8 - 4)
+                                   : n;
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (n < N) v = *(const u32x4*)(w + n * Kin + k);
+    if (n < N) v = *(const u32x4*)(w + src * Kin + k);
     *(u32x4*)(out + p * 8) = v;
 }
 
@@ -441,8 +481,10 @@ size_t orthrus_packed_weight_bytes(int N, int Kin)
     return (size_t)blocks * kWTileRows * (size_t)Kin * sizeof(uint16_t);
 }
 
-int orthrus_pack_weight(const void *w, int N, int Kin, void *packed, size_t packed_bytes,
-                        hipStream_t stream)
+namespace {
+
+int pack(const void *w, int N, int Kin, int pair_I, void *packed, size_t packed_bytes,
+         hipStream_t stream)
 {
     if (!w || !packed) return ORTHRUS_ERR_NULL;
     if (N < 1 || Kin < 1) return ORTHRUS_ERR_SHAPE;
@@ -453,9 +495,26 @@ int orthrus_pack_weight(const void *w, int N, int Kin, void *packed, size_t pack
     if (packed_bytes < need) return ORTHRUS_ERR_WORKSPACE;
     const int64_t pieces = (int64_t)(need / 16);
     hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0,
-                       stream, static_cast<const uint16_t *>(w), N, Kin, pieces,
+                       stream, static_cast<const uint16_t *>(w), N, Kin, pieces, pair_I,
                        static_cast<uint16_t *>(packed));
     return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+}  // namespace
+
+int orthrus_pack_weight(const void *w, int N, int Kin, void *packed, size_t packed_bytes,
+                        hipStream_t stream)
+{
+    return pack(w, N, Kin, 0, packed, packed_bytes, stream);
+}
+
+int orthrus_pack_weight_gate_up(const void *w, int I, int Kin, void *packed,
+                                size_t packed_bytes, hipStream_t stream)
+{
+    if (!w || !packed) return ORTHRUS_ERR_NULL;
+    if (I < 1 || I > (1 << 30)) return ORTHRUS_ERR_SHAPE;
+    if (I % 4) return ORTHRUS_ERR_UNSUPPORTED;
+    return pack(w, 2 * I, Kin, I, packed, packed_bytes, stream);
 }
 
 namespace {
@@ -627,11 +686,12 @@ int launch_qk(const float *qkv, int S, const void *q_norm, const void *k_norm,
     return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }
 
-int launch_swiglu(const float *gu, int S, void *act, int R, int I, hipStream_t stream)
+int launch_swiglu(const float *gu, int S, void *act, int R, int I, int paired,
+                  hipStream_t stream)
 {
     const int64_t total = (int64_t)R * (I / 4);
     hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       gu, S, static_cast<uint16_t *>(act), R, I);
+                       gu, S, static_cast<uint16_t *>(act), R, I, paired);
     return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }
 
@@ -672,7 +732,7 @@ int orthrus_swiglu(const float *gate_up, void *act, int R, int I, hipStream_t st
     if (!gate_up || !act) return ORTHRUS_ERR_NULL;
     if (R < 1 || I < 1) return ORTHRUS_ERR_SHAPE;
     if (I % 4 || mis16(gate_up) || mis8(act)) return ORTHRUS_ERR_UNSUPPORTED;
-    return launch_swiglu(gate_up, 1, act, R, I, stream);
+    return launch_swiglu(gate_up, 1, act, R, I, 0, stream);
 }
 
 int orthrus_gemm_swiglu(const void *x, const void *w_gate_up, void *act, int R, int I, int Kin,
@@ -686,10 +746,12 @@ int orthrus_gemm_swiglu(const void *x, const void *w_gate_up, void *act, int R, 
     if ((st = partial_check(workspace, workspace_bytes, R, 2 * I, Kin)) != ORTHRUS_OK) return st;
     const int S = gemm_splits(2 * I, Kin);
     float *part = static_cast<float *>(workspace);
+    // not split: SwiGLU in the projection's own epilogue, no partial sums
+    if (S == 1) return gemm_main(x, w_gate_up, R, 2 * I, Kin, 1, 3, nullptr, act, nullptr, stream);
     if ((st = gemm_main(x, w_gate_up, R, 2 * I, Kin, S, 0, part, nullptr, nullptr, stream)) !=
         ORTHRUS_OK)
         return st;
-    return launch_swiglu(part, S, act, R, I, stream);
+    return launch_swiglu(part, S, act, R, I, 1, stream);
 }
 
 int orthrus_block_tokens(const int32_t *anchor, const int32_t *cand, int32_t fill,

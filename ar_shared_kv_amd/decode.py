@@ -63,7 +63,10 @@ class DecodeModel:
         self.w = {}
         for k, v in weights.items():
             t = v.to(dev).contiguous()
-            self.w[k] = api.pack_weight(t) if k.endswith(_PACKED) else t
+            if k.endswith(".wgu"):
+                self.w[k] = api.pack_weight_gate_up(t)   # SwiGLU in the projection
+            else:
+                self.w[k] = api.pack_weight(t) if k.endswith(_PACKED) else t
         d = dims
         self.mask_token = d.V                      # the extra embedding row
         R = B * max(K, PREFILL_CHUNK)              # rows of the largest block

@@ -382,6 +382,16 @@ int orthrus_pack_weight(const void *w, int N, int Kin, void *packed,
  * multiple of 64. */
 size_t orthrus_packed_weight_bytes(int N, int Kin);
 
+/* orthrus_pack_weight_gate_up -- the MLP's gate/up weight w bf16 [2I][Kin]
+ * (the I gate rows, then the I up rows) packed for orthrus_gemm_swiglu: as
+ * orthrus_pack_weight of the 2I rows reordered so that every 8 rows are gate
+ * rows 4g..4g+3 and then up rows I+4g..I+4g+3 (g = row / 8).  Each 128-row
+ * block then holds 64 outputs' gate and up rows, and an unsplit projection
+ * applies SwiGLU in its own epilogue.  I a multiple of 4; packed holds
+ * orthrus_packed_weight_bytes(2I, Kin) bytes. */
+int orthrus_pack_weight_gate_up(const void *w, int I, int Kin, void *packed,
+                                size_t packed_bytes, hipStream_t stream);
+
 /*
  * orthrus_gemm -- y = x W^T (+ residual): x bf16 [R][Kin], W bf16 [N][Kin]
  * (a linear layer's weight, one row per output) in the packed tile layout of
@@ -409,8 +419,8 @@ int orthrus_rmsnorm(const float *x, const void *weight, void *y, int R, int H,
  * fused into the second pass that adds the partial sums of the split input
  * dimension.  Each gives, bit for bit, what orthrus_gemm (fp32 output)
  * followed by the separate kernel gives: the partial sums are added in split
- * order and the epilogue's arithmetic is the separate kernel's.  They always
- * write the partial sums (also when the input dimension is not split), so
+ * order and the epilogue's arithmetic is the separate kernel's.  They may
+ * write partial sums also when the input dimension is not split, so
  * workspace >= orthrus_gemm_epilogue_workspace_bytes(R, N, Kin) bytes,
  * 16-byte aligned, with N the projection's output width.  Same x / W
  * contract as orthrus_gemm (W packed by orthrus_pack_weight, Kin a multiple
@@ -429,10 +439,13 @@ int orthrus_gemm_rmsnorm(const void *x, const void *w, float *h,
                          size_t workspace_bytes, hipStream_t stream);
 
 /* orthrus_gemm_swiglu -- the MLP's gate/up projection and SwiGLU: W bf16
- * [2I][Kin] (the I gate rows, then the I up rows), act bf16 [R][I] =
- * orthrus_gemm(x, W, NULL, gu, R, 2I, Kin, F32) then orthrus_swiglu(gu, act,
- * R, I), without the fp32 gu ever being written.  I a multiple of 4; act
- * 8-byte aligned. */
+ * [2I][Kin] (the I gate rows, then the I up rows) packed by
+ * orthrus_pack_weight_gate_up, act bf16 [R][I] = orthrus_gemm(x, W, NULL, gu,
+ * R, 2I, Kin, F32) (W packed by orthrus_pack_weight) then orthrus_swiglu(gu,
+ * act, R, I), without the fp32 gu ever being written.  When the input
+ * dimension is not split (the Qwen3-8B MLP: 2I = 24,576 rows) it is one
+ * launch that applies SwiGLU in its epilogue.  I a multiple of 4; act 8-byte
+ * aligned. */
 int orthrus_gemm_swiglu(const void *x, const void *w_gate_up, void *act, int R,
                         int I, int Kin, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);

@@ -304,6 +304,13 @@ def test_pack_weight_sizes_and_validation():
     assert P(FAKE + 8, 132, 64, FAKE, need, None) == B.ERR_UNSUPPORTED
     assert P(FAKE, 132, 64, FAKE + 8, need, None) == B.ERR_UNSUPPORTED
     assert P(FAKE, 132, 64, FAKE, need - 2, None) == B.ERR_WORKSPACE
+    G = B.lib().orthrus_pack_weight_gate_up
+    need = pb(2 * 132, 64)
+    assert G(None, 132, 64, FAKE, need, None) == B.ERR_NULL
+    assert G(FAKE, 0, 64, FAKE, need, None) == B.ERR_SHAPE
+    assert G(FAKE, 130, 64, FAKE, need, None) == B.ERR_UNSUPPORTED    # I not a multiple of 4
+    assert G(FAKE, 132, 96, FAKE, need, None) == B.ERR_UNSUPPORTED    # Kin not a multiple of 64
+    assert G(FAKE, 132, 64, FAKE, need - 2, None) == B.ERR_WORKSPACE
 
 
 def test_single_hip_runtime_in_process():

@@ -78,6 +78,24 @@ def test_pack_weight_is_the_tile_permutation(N, Kin):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("I,Kin", [(12288, 64), (132, 64), (4, 128)])
+def test_pack_weight_gate_up_pairs_gate_and_up_rows(I, Kin):
+    """Every 8 packed rows are gate rows 4g..4g+3 and then up rows
+    I+4g..I+4g+3, packed as orthrus_pack_weight packs; bit for bit."""
+    gen = torch.Generator().manual_seed(I + Kin)
+    w = bf((2 * I, Kin), gen)
+    pw = api.pack_weight_gate_up(w.to(DEV))
+    torch.cuda.synchronize()
+    g = np.arange(2 * I) // 8
+    j = np.arange(2 * I) % 8
+    src = np.where(j < 4, 4 * g + j, I + 4 * g + j - 4)
+    paired = w[torch.from_numpy(src)].contiguous()
+    ref = api.pack_weight(paired.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(pw.data, ref.data)
+    assert pw.gate_up and not ref.gate_up
+
+
 def test_gemm_rows_do_not_depend_on_the_batch():
     gen = torch.Generator().manual_seed(3)
     x, w = bf((32, 4096), gen), bf((6144, 4096), gen, 4096 ** -0.5)
@@ -192,10 +210,18 @@ def test_gemm_rmsnorm_equals_gemm_then_rmsnorm(R, H, Kin):
     assert (err <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max()).all()
 
 
-@pytest.mark.parametrize("R,I,Kin", [(32, 12288, 4096), (7, 132, 64), (40, 1024, 512)])
+@pytest.mark.parametrize("R,I,Kin", [
+    (32, 12288, 4096),     # the Qwen3-8B MLP: not split, SwiGLU in the projection's epilogue
+    (7, 132, 64),          # not split, ragged last block (264 rows in 3 blocks)
+    (40, 1024, 512),       # split 2 ways: paired partial sums, separate SwiGLU pass
+    (100, 256, 4096),      # 128-row work-groups, split 16 ways
+    (70, 96, 128),         # 128-row work-groups, not split, one ragged block
+])
 def test_gemm_swiglu_equals_gemm_then_swiglu(R, I, Kin):
     gen = torch.Generator().manual_seed(R + I + Kin)
-    x, w = bf((R, Kin), gen).to(DEV), api.pack_weight(bf((2 * I, Kin), gen, Kin ** -0.5).to(DEV))
+    wr = bf((2 * I, Kin), gen, Kin ** -0.5).to(DEV)
+    x, w = bf((R, Kin), gen).to(DEV), api.pack_weight(wr)
+    wp = api.pack_weight_gate_up(wr)
     say(f"gemm_swiglu R={R} I={I} Kin={Kin}")
     gu = torch.empty((R, 2 * I), dtype=torch.float32, device=DEV)
     ws = _ws(B_.orthrus_gemm_workspace_bytes(R, 2 * I, Kin))
@@ -204,7 +230,7 @@ def test_gemm_swiglu_equals_gemm_then_swiglu(R, I, Kin):
     B_.check("swiglu", B_.orthrus_swiglu(gu, a1, R, I))
     a2 = torch.empty_like(a1)
     ws2 = _ws(B_.orthrus_gemm_epilogue_workspace_bytes(R, 2 * I, Kin))
-    B_.check("gemm_swiglu", B_.orthrus_gemm_swiglu(x, w, a2, R, I, Kin, ws2, ws2.numel()))
+    B_.check("gemm_swiglu", B_.orthrus_gemm_swiglu(x, wp, a2, R, I, Kin, ws2, ws2.numel()))
     torch.cuda.synchronize()
     assert torch.equal(a1, a2)
 

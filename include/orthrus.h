@@ -27,10 +27,13 @@
  *  - Return value: ORTHRUS_OK or an orthrus_status code;
  *    orthrus_status_string() names it.  ORTHRUS_ERR_LAUNCH reports a HIP
  *    launch error (hipGetLastError after the launch).
- *  - No global mutable state: concurrent calls on different streams are
+ *  - No global mutable state (but for the static scratch array of
+ *    orthrus_block_attn_noalloc): concurrent calls on different streams are
  *    safe as long as their outputs and workspaces do not overlap.
- *  - Tensors are dense, row-major, in the shapes given below; element type
- *    `dtype` is ORTHRUS_F32 (float) or ORTHRUS_BF16 (bfloat16).
+ *  - Tensors are dense, row-major, in the shapes given below, except the
+ *    weight matrices of the projections and the LM head, which are read in
+ *    the packed tile layout of orthrus_pack_weight; element type `dtype` is
+ *    ORTHRUS_F32 (float) or ORTHRUS_BF16 (bfloat16).
  */
 #ifndef ORTHRUS_H
 #define ORTHRUS_H

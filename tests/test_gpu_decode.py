@@ -199,3 +199,62 @@ def test_orthrus_loop_equals_greedy_on_gpu_and_oracle():
     say(f"  GPU greedy == oracle greedy for the first {agree.tolist()} tokens")
     record("decode-loop", "GPU greedy vs oracle greedy", agreeing_prefix=agree.tolist())
     assert agree.min() >= 8
+
+
+def test_orthrus_step_graph_replays_match_eager():
+    """One whole Orthrus step (two layers, both views, the fused LM head,
+    consensus, the multi-layer append) captured in a HIP graph: every replay,
+    with its outputs scrambled and the step's inputs restored by eager work
+    in between, reproduces the eager step bit for bit."""
+    d = Dims(H=512, Hq=4, Hkv=2, D=128, I=1024, V=1000, layers=2)
+    w = W.model_weights(dims_of(d), seed=21)
+    B, K, L = 2, 8, 40
+    gm = DecodeModel(d, w, B, K, L + K, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(22)
+    gm.kc.copy_(torch.randn(gm.kc.shape, generator=g, device=DEV).to(torch.bfloat16))
+    gm.vc.copy_(torch.randn(gm.vc.shape, generator=g, device=DEV).to(torch.bfloat16))
+    gm.set_lengths(L)
+    anchor0 = torch.tensor([7, 11], dtype=torch.int32, device=DEV)
+
+    def prepare():
+        gm.anchor.copy_(anchor0)
+        gm.kc[:, :, :, L:].fill_(float("nan"))
+        gm.vc[:, :, :, L:].fill_(float("nan"))
+        for t in (gm.n_emit, gm.emit_off, gm.emitted, gm.d_tok, gm.a_tok):
+            t.fill_(-7)
+        gm.kb.fill_(float("nan"))
+        gm.vb.fill_(float("nan"))
+        gm.x.fill_(float("nan"))
+        if hasattr(gm, "lens_next"):
+            gm.lens_next.fill_(-7)
+
+    def results():
+        n = gm.n_emit.cpu().tolist()
+        r = {k: getattr(gm, k).clone() for k in ("n_emit", "emit_off", "d_tok", "a_tok", "anchor",
+                                                  "lens_next")}
+        r["emitted"] = gm.emitted[: int(gm.emit_off[-1])].clone()
+        r["kb"], r["vb"] = gm.kb.view(torch.int16).clone(), gm.vb.view(torch.int16).clone()
+        r["x"] = gm.x[: B * K].view(torch.int16).clone()
+        for b in range(B):
+            r[f"kc{b}"] = gm.kc[:, b, :, L:L + n[b]].view(torch.int16).clone()
+            r[f"vc{b}"] = gm.vc[:, b, :, L:L + n[b]].view(torch.int16).clone()
+        return r
+
+    prepare()
+    gm.orthrus_step(advance=False)
+    torch.cuda.synchronize()
+    ref = results()
+    say(f"graph decode step: eager n_emit {ref['n_emit'].tolist()}")
+    assert int(gm.lens.max()) == L                          # the replayable form leaves lens
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        gm.orthrus_step(advance=False)
+    for rep in range(3):
+        prepare()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        got = results()
+        say(f"graph decode step: replay {rep}")
+        for k, v in ref.items():
+            assert torch.equal(got[k], v), (rep, k)

@@ -512,7 +512,7 @@ int orthrus_pack_weight_gate_up(const void *w, int I, int Kin, void *packed,
                                 size_t packed_bytes, hipStream_t stream)
 {
     if (!w || !packed) return ORTHRUS_ERR_NULL;
-    if (I < 1 || I > (1 << 30)) return ORTHRUS_ERR_SHAPE;
+    if (I < 1 || I > INT32_MAX / 2) return ORTHRUS_ERR_SHAPE;      // 2I rows must fit an int
     if (I % 4) return ORTHRUS_ERR_UNSUPPORTED;
     return pack(w, 2 * I, Kin, I, packed, packed_bytes, stream);
 }
@@ -669,7 +669,7 @@ int qk_check(const void *q_norm, const void *k_norm, const int32_t *lens, int K,
     if (!q_norm || !k_norm || !lens || !q || !k || !v) return ORTHRUS_ERR_NULL;
     if (R < 1 || K < 1 || R % K || Hq < 1 || Hkv < 1 || !(eps > 0.f) || !(rope_theta > 1.f))
         return ORTHRUS_ERR_SHAPE;
-    if (D != 128) return ORTHRUS_ERR_UNSUPPORTED;
+    if (D != 128 || Hq > 65536 || Hkv > 65536) return ORTHRUS_ERR_UNSUPPORTED;
     return ORTHRUS_OK;
 }
 
@@ -730,8 +730,9 @@ int orthrus_gemm_qk_norm_rope(const void *x, const void *w_qkv, const void *q_no
 int orthrus_swiglu(const float *gate_up, void *act, int R, int I, hipStream_t stream)
 {
     if (!gate_up || !act) return ORTHRUS_ERR_NULL;
-    if (R < 1 || I < 1) return ORTHRUS_ERR_SHAPE;
+    if (R < 1 || I < 1 || I > INT32_MAX / 2) return ORTHRUS_ERR_SHAPE;
     if (I % 4 || mis16(gate_up) || mis8(act)) return ORTHRUS_ERR_UNSUPPORTED;
+    if ((int64_t)R * (I / 4) > (int64_t)INT32_MAX * 256) return ORTHRUS_ERR_UNSUPPORTED;
     return launch_swiglu(gate_up, 1, act, R, I, 0, stream);
 }
 
@@ -739,7 +740,7 @@ int orthrus_gemm_swiglu(const void *x, const void *w_gate_up, void *act, int R, 
                         void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (!act) return ORTHRUS_ERR_NULL;
-    if (I < 1) return ORTHRUS_ERR_SHAPE;
+    if (I < 1 || I > INT32_MAX / 2) return ORTHRUS_ERR_SHAPE;     // 2I rows must fit an int
     int st = gemm_check(x, w_gate_up, R, 2 * I, Kin);
     if (st != ORTHRUS_OK) return st;
     if (I % 4 || mis8(act)) return ORTHRUS_ERR_UNSUPPORTED;

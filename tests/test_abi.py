@@ -272,6 +272,7 @@ def test_layer_validation_codes():
     need = ew(32, 24576, 4096)
     assert sw(FAKE, FAKE, None, 32, 12288, 4096, FAKE, need, None) == B.ERR_NULL
     assert sw(FAKE, FAKE, FAKE, 32, 0, 4096, FAKE, need, None) == B.ERR_SHAPE
+    assert sw(FAKE, FAKE, FAKE, 32, 1 << 30, 4096, FAKE, need, None) == B.ERR_SHAPE  # 2I overflows
     assert sw(FAKE, FAKE, FAKE, 32, 12286, 4096, FAKE, need, None) == B.ERR_UNSUPPORTED
     assert sw(FAKE, FAKE, FAKE, 32, 12288, 4096, FAKE, need - 1, None) == B.ERR_WORKSPACE
     qk = L.orthrus_gemm_qk_norm_rope
@@ -284,6 +285,8 @@ def test_layer_validation_codes():
     assert qk(*bad) == B.ERR_SHAPE                               # R not a multiple of K
     bad = list(args); bad[12] = 64
     assert qk(*bad) == B.ERR_UNSUPPORTED                         # D = 128 only
+    bad = list(args); bad[10] = 1 << 20
+    assert qk(*bad) == B.ERR_UNSUPPORTED                         # absurd head counts
     bad = list(args); bad[17] = need - 4
     assert qk(*bad) == B.ERR_WORKSPACE
 
@@ -308,6 +311,7 @@ def test_pack_weight_sizes_and_validation():
     need = pb(2 * 132, 64)
     assert G(None, 132, 64, FAKE, need, None) == B.ERR_NULL
     assert G(FAKE, 0, 64, FAKE, need, None) == B.ERR_SHAPE
+    assert G(FAKE, 1 << 30, 64, FAKE, need, None) == B.ERR_SHAPE       # 2I would overflow an int
     assert G(FAKE, 130, 64, FAKE, need, None) == B.ERR_UNSUPPORTED    # I not a multiple of 4
     assert G(FAKE, 132, 96, FAKE, need, None) == B.ERR_UNSUPPORTED    # Kin not a multiple of 64
     assert G(FAKE, 132, 64, FAKE, need - 2, None) == B.ERR_WORKSPACE

@@ -10,7 +10,7 @@
 // gemm_kernel: y[r][n] = sum_k x[r][k] * w[n][k] for the few rows of a
 // decode block (R = B*K) against a weight of N rows: HBM-bound (the weight
 // is read once), so the weight streams HBM -> LDS with global_load_lds
-// through a 3-slot ring, like the LM head.  A work-group covers 128 weight
+// through a ring (4 slots at 32 rows, 3 at 64, 2 at 128), like the LM head.  A work-group covers 128 weight
 // rows and RB hidden rows; when the N/128 blocks cannot fill the chip the
 // input dimension is split S ways (S depends on N and the input size only)
 // and a second launch adds the fp32 partial sums in split order.  Every
@@ -540,8 +540,9 @@ int gemm_main(const void* x, const void* w, int R, int N, int Kin, int S, int mo
     const int cps = Kin / kGemmHC / S;
     const uint16_t *xp = static_cast<const uint16_t*>(x), *wp = static_cast<const uint16_t*>(w);
     const unsigned gx = (unsigned)((N + kGemmNB - 1) / kGemmNB);
-    if (R <= 32)
-        hipLaunchKernelGGL((gemm_kernel<3, 32>), dim3(gx, 1, S), dim3(256), 0, stream, xp, wp, R,
+    if (R <= 32)   // three chunks in flight: the Qwen3-8B layer's projections 94.4 against
+                   // 96.3 us with two (a work-group streams only 8 to 64 chunks), 97.1 with five
+        hipLaunchKernelGGL((gemm_kernel<4, 32>), dim3(gx, 1, S), dim3(256), 0, stream, xp, wp, R,
                            N, Kin, cps, mode, part, y, res);
     else if (R <= 64)
         hipLaunchKernelGGL((gemm_kernel<3, 64>), dim3(gx, 1, S), dim3(256), 0, stream, xp, wp, R,
